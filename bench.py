@@ -1,0 +1,237 @@
+#!/usr/bin/env python
+"""PBSA benchmark on one MI355X.
+
+Workload (one step = one chunk of a streaming rollout in steady state):
+the Wan2.1-T2V-1.3B-shaped chunk - 30 layers, each with 12 heads of 128, a
+4680-token chunk (37 blocks of 128, the last 72 tokens), a window of the two
+previous chunks (74 slots), a full persistent pool of 32 blocks and top-16
+window selection.  Per layer: pbsa_select -> pbsa_attn_fwd ->
+pbsa_memory_update (the 37 blocks of chunk t-2 leave the window) ->
+pbsa_window_append (chunk t takes their slots).  Inputs are synthetic
+(seeded, generated on the device) and resident in HBM before timing.
+
+Prints ONE JSON line: attention TFLOP/s over the whole step (algorithmic
+forward FLOPs 4*d*sum_rows|U_r| / step time), per-chunk latency, the forward
+kernel's roofline position (HIP events around every forward launch inside
+the timed region), a training step (batch 2, fwd + bwd) and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_rollout(n_layers, device):
+    import pbsa_synth as syn
+    from block_sparse_attention_20_amd.rollout import Rollout
+    s = syn.WAN_CHUNK
+    ro = Rollout(n_layers, s.B, s.H, s.d, s.T, s.Nq, s.C, s.topk, window_chunks=2, device=device)
+    for l in range(n_layers):
+        st = syn.wan_chunk_state(l, device=device)
+        ro.layers[l].load(st)
+    # generator ids: pool 0..31, window = chunks 2 and 3 -> the current chunk is 4
+    ro.t = 4
+    return ro
+
+
+def time_steps(ro, steps, warmup, torch):
+    """Whole-step timing + HIP events around each forward launch."""
+    n_layers = len(ro.layers)
+    for _ in range(warmup):
+        ro.run_chunk()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_layers)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        t = ro.t
+        for l, L in enumerate(ro.layers):
+            L.select()
+            ev[s][l][0].record()
+            L.fwd()
+            ev[s][l][1].record()
+            if t >= ro.window_chunks:
+                L.update(ro.leaving[t % ro.window_chunks], ro.n_sink)
+            L.append_window(ro.first_slot(t), t * ro.QB)
+        ro.advance()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    fwd_ms = [a.elapsed_time(b) for row in ev for a, b in row]
+    return (t1 - t0) * 1e3 / steps, fwd_ms
+
+
+def breakdown(ro, torch, reps=3):
+    """Average device time of each call (separate, untimed pass)."""
+    names = ("select", "fwd", "update", "append")
+    acc = {n: [] for n in names}
+    for _ in range(reps):
+        t = ro.t
+        for L in ro.layers:
+            calls = (L.select, L.fwd,
+                     lambda: L.update(ro.leaving[t % ro.window_chunks], ro.n_sink),
+                     lambda: L.append_window(ro.first_slot(t), t * ro.QB))
+            for n, fn in zip(names, calls):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(); fn(); b.record()
+                acc[n].append((a, b))
+        ro.advance()
+    torch.cuda.synchronize()
+    return {n: round(1e3 * sum(a.elapsed_time(b) for a, b in v) / len(v), 2) for n, v in acc.items()}
+
+
+def train_step(torch, steps=5, warmup=2, device="cuda"):
+    """Batch-2 training step of one layer: select + fwd + bwd."""
+    import pbsa_synth as syn
+    from block_sparse_attention_20_amd.layer import PBSALayer
+    from block_sparse_attention_20_amd.rollout import attended_tokens
+    s = syn.WAN_TRAIN
+    L = PBSALayer(s.B, s.H, s.d, s.T, s.Nq, s.W, s.C, s.topk, device=device)
+    st = syn.make_state(s, 4000, sigma=1 / math.sqrt(s.d), shift=1.5, n_planted=8,
+                        win_len=syn.chunk_window_lens(s.Nq, s.T, 2), device=device)
+    L.load(st)
+    dout = syn.make_dout(s, 4001, device=device)
+    grads = None
+    for _ in range(warmup):
+        L.select(); L.fwd(); grads = L.bwd(dout, grads)
+    torch.cuda.synchronize()
+    ef = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    eb = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        L.select()
+        ef[i][0].record(); L.fwd(); ef[i][1].record()
+        eb[i][0].record(); grads = L.bwd(dout, grads); eb[i][1].record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    pairs = attended_tokens(L)
+    fwd_ms = sum(a.elapsed_time(b) for a, b in ef) / steps
+    bwd_ms = sum(a.elapsed_time(b) for a, b in eb) / steps
+    fwd_f, bwd_f = 4 * s.d * pairs, 10 * s.d * pairs
+    return {"workload": "wan chunk training step, batch 2 (select + fwd + bwd, one layer)",
+            "ms_per_step": round(ms, 4), "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "fwd_gflop": round(fwd_f / 1e9, 2), "bwd_gflop": round(bwd_f / 1e9, 2),
+            "tflops": round((fwd_f + bwd_f) / (ms * 1e-3) / 1e12, 2),
+            "bwd_tflops": round(bwd_f / (bwd_ms * 1e-3) / 1e12, 2),
+            "bwd_flop_convention": "10*d per attended (row, token) pair, QK^T recompute included"}
+
+
+def cpu_baseline(ro, budget_s, torch):
+    """The fp64 oracle (as it stands) on a bounded sample of the same
+    workload: layer 0's select over every head, then the forward of as many
+    query blocks as fit in the time budget.  Reported in the metric's unit."""
+    import numpy as np
+    from oracle import pbsa_oracle as po
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    L = ro.layers[0]
+    st = {k: L.t[k].detach().cpu() for k in ("q", "k_cur", "v_cur", "k_win", "v_win", "win_len",
+                                                "win_id", "k_pool", "v_pool", "pool_len", "pool_id",
+                                                "pool_count")}
+    st = po.as_f64_state(st)
+    scale = 1 / math.sqrt(L.d)
+    t0 = time.perf_counter()
+    r = po.select(st, L.topk, scale, L.T)
+    t_sel = time.perf_counter() - t0
+    blocks, flops = [], 0
+    t0 = time.perf_counter()
+    QB, H = L.QB, L.H
+    order = [(0, h, i) for i in range(QB) for h in range(H)]
+    for b, h, i in order:
+        po.attn_fwd(st, r["sel"], r["sel_count"], scale, L.T, blocks=[(b, h, i)])
+        rows = min(L.T, L.Nq - i * L.T)
+        n_u = sum(int(st["pool_len"][b, h, p]) for p in range(int(st["pool_count"][b, h])))
+        n_u += sum(int(st["win_len"][w]) for w in r["sel"][b, h, i, :r["sel_count"][b, h, i]])
+        n_u += L.Nq
+        flops += 4 * L.d * rows * n_u
+        blocks.append((h, i))
+        if time.perf_counter() - t0 > budget_s:
+            break
+    t_fwd = time.perf_counter() - t0
+    return {"value": round(flops / t_fwd / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"layer 0 of the Wan chunk: coarse routing of all 12 heads ({t_sel:.1f} s), "
+                      f"then the fp64 forward of {len(blocks)} of {QB * H} (head, query block) "
+                      f"pairs ({t_fwd:.1f} s); value = forward FLOPs / forward time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=30)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle forward work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-train", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: PBSA shards by head with no exchange, and this build "
+              "runs on a single MI355X (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import block_sparse_attention_20_amd as pkg
+    from block_sparse_attention_20_amd.rollout import attended_tokens
+    pkg.lib()
+    dev = "cuda"
+    log(f"building 30-layer state ({args.layers} layers)")
+    ro = build_rollout(args.layers, dev)
+    torch.cuda.synchronize()
+    log("timing")
+    ms, fwd_ms = time_steps(ro, args.steps, args.warmup, torch)
+    d = ro.layers[0].d
+    flops_layer = [4 * d * attended_tokens(L) for L in ro.layers]
+    step_flops = sum(flops_layer)
+    value = step_flops / (ms * 1e-3) / 1e12
+    fwd_avg_ms = sum(fwd_ms) / len(fwd_ms)
+    fwd_tflops = (step_flops / len(ro.layers)) / (fwd_avg_ms * 1e-3) / 1e12
+    bd = breakdown(ro, torch)
+    out = {
+        "metric": "PBSA attention TFLOP/s and per-chunk latency (ms) on one MI355X; % of MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "wan2.1-t2v-1.3b-shaped chunk, steady-state rollout step: "
+                               f"{args.layers} layers x (select + fwd + update + append)",
+                   "layers": args.layers, "heads": 12, "head_dim": d, "block": 128,
+                   "chunk_tokens": 4680, "window_slots": 74, "pool_blocks": 32, "topk": 16,
+                   "parallelism": "1 GPU"},
+        "per_chunk_latency_ms": round(ms, 4),
+        "fwd_gflop_per_layer": round(step_flops / len(ro.layers) / 1e9, 2),
+        "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"kernel": "attn_fwd_bf16_kernel<128,128>", "bound": "mfma",
+                     "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "launch_us": round(fwd_avg_ms * 1e3, 2),
+                     "launches": len(fwd_ms)},
+        "breakdown_us_per_layer": bd,
+    }
+    if not args.no_train:
+        log("training step")
+        out["train"] = train_step(torch)
+    if not args.no_cpu_baseline:
+        log("cpu baseline")
+        out["cpu_baseline"] = cpu_baseline(ro, args.cpu_budget, torch)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,48 @@
+// Device helpers shared by the PBSA kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pbsa.h"
+
+namespace pbsa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// bf16 bits -> fp32 (exact)
+__device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+__device__ __forceinline__ float bflo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bfhi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+}
+
+__device__ __forceinline__ void set_status(int32_t *st, int bit) {
+  if (st) atomicOr(st, bit);
+}
+
+// Total order of the routing decisions: larger score first, then smaller id,
+// NaN after every number (NaNs among themselves by id).
+__device__ __forceinline__ bool ranks_before(float sa, int64_t ida, float sb, int64_t idb) {
+  bool na = sa != sa, nb = sb != sb;
+  if (na != nb) return nb;
+  if (!na && sa != sb) return sa > sb;
+  return ida < idb;
+}
+
+}  // namespace pbsa

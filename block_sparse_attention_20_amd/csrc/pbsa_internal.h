@@ -1,0 +1,38 @@
+// Internal launcher declarations shared by the PBSA host code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pbsa.h"
+
+namespace pbsa {
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t select_ws_bytes(const pbsa_problem &p);
+size_t select_lds_bytes(const pbsa_problem &p);
+size_t update_ws_bytes(const pbsa_problem &p);
+size_t bwd_ws_bytes(const pbsa_problem &p);
+
+hipError_t launch_select(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
+                         int32_t *sel, int32_t *sel_count, float *mass_pool, float *mass_win,
+                         void *ws, hipStream_t st);
+hipError_t launch_block_mean(const pbsa_problem &p, const void *x, const int32_t *len,
+                             int64_t n_blocks, float *out, hipStream_t st);
+hipError_t launch_window_append(const pbsa_problem &p, const pbsa_kv &kv, void *k_win, void *v_win,
+                                float *kbar_win, int32_t *win_len, int64_t *win_id,
+                                int first_slot, int64_t first_id, hipStream_t st);
+hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
+                           const int32_t *sel, const int32_t *sel_count, void *o, float *lse,
+                           hipStream_t st);
+hipError_t launch_attn_bwd(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
+                           const int32_t *sel, const int32_t *sel_count, const void *o,
+                           const float *lse, const void *dout, void *dq, const pbsa_kv_grad &g,
+                           void *ws, hipStream_t st);
+hipError_t launch_memory_update(const pbsa_problem &p, const pbsa_kv &kv, const float *mass_pool,
+                                const float *mass_win, const int32_t *leaving, int n_leave,
+                                int64_t n_sink, void *ws, hipStream_t st);
+
+}  // namespace pbsa

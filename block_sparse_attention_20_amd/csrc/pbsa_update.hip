@@ -1,0 +1,203 @@
+// PBSA persistent-memory update: Top-C retention with pinned sinks, slot
+// placement, and bit-exact block copies.
+//
+// Method: "Sparse Forcing: Native Trainable Sparse Attention for Real-time
+// Autoregressive Diffusion Video Generation" (gist.science/es explainer,
+// sec. 2 "Arquitectura Propuesta": the persistent memory holds sink blocks
+// (fixed global anchors) and dynamic blocks chosen by coarse scoring; Top-C
+// retention keeps the C best-scored blocks and discards the less relevant
+// blocks leaving the local window).  The kernel is the "selective cache
+// update" the same page credits the PBSA kernel with.
+//
+// Two launches: a decision kernel per (b, h) that ranks the candidates and
+// computes where each admitted block goes, and an HBM-bound copy kernel
+// (one workgroup per admitted block) that moves K/V/kbar.
+#include "pbsa_common.h"
+#include "pbsa_internal.h"
+
+namespace pbsa {
+
+constexpr int kMaxC = 1024;
+constexpr int kMaxLeave = 1024;
+constexpr int kMaxX = kMaxC + kMaxLeave;
+
+__global__ __launch_bounds__(256) void update_decide_kernel(
+    const float *__restrict__ mass_pool, const float *__restrict__ mass_win,
+    const int32_t *__restrict__ leaving, int n_leave, const int32_t *__restrict__ win_len,
+    const int64_t *__restrict__ win_id, int32_t *__restrict__ pool_len,
+    int64_t *__restrict__ pool_id, int32_t *__restrict__ pool_count, int32_t *__restrict__ a_slot,
+    int32_t *__restrict__ a_src, int32_t *__restrict__ a_count, int H, int W, int C, int T,
+    int64_t n_sink, int32_t *status) {
+  __shared__ int64_t xid[kMaxX];
+  __shared__ float xm[kMaxX];
+  __shared__ int32_t xsrc[kMaxX];   // >= 0: pool slot; < 0: window slot -1-w
+  __shared__ int8_t xkeep[kMaxX];
+  __shared__ int8_t cflag[kMaxLeave];
+  __shared__ int32_t free_slot[kMaxC];
+  __shared__ int red[4];
+
+  const int t = threadIdx.x;
+  const size_t bh = (size_t)blockIdx.y * H + blockIdx.x;
+  int n_pool = pool_count[bh];
+  if (n_pool < 0 || n_pool > C) {
+    if (t == 0) set_status(status, PBSA_STATUS_POOL_COUNT);
+    n_pool = max(0, min(n_pool, C));
+  }
+  for (int p = t; p < n_pool; p += 256) {
+    xid[p] = pool_id[bh * C + p];
+    xm[p] = mass_pool[bh * C + p];
+    xsrc[p] = p;
+  }
+  __syncthreads();
+  // candidate filter: slot in range, non-empty, not pooled, first of its id
+  for (int c = t; c < n_leave; c += 256) {
+    const int w = leaving[c];
+    bool ok = w >= 0 && w < W;
+    if (!ok) set_status(status, PBSA_STATUS_SEL);
+    int64_t id = 0;
+    if (ok) {
+      ok = win_len[w] > 0;
+      id = win_id[w];
+    }
+    for (int p = 0; ok && p < n_pool; ++p) ok = xid[p] != id;
+    for (int c2 = 0; ok && c2 < c; ++c2) {
+      const int w2 = leaving[c2];
+      if (w2 >= 0 && w2 < W && win_len[w2] > 0 && win_id[w2] == id) ok = false;
+    }
+    cflag[c] = ok ? 1 : 0;
+  }
+  __syncthreads();
+  for (int c = t; c < n_leave; c += 256) {
+    if (!cflag[c]) continue;
+    int pos = n_pool;
+    for (int c2 = 0; c2 < c; ++c2) pos += cflag[c2];
+    const int w = leaving[c];
+    xid[pos] = win_id[w];
+    xm[pos] = mass_win[bh * W + w];
+    xsrc[pos] = -1 - w;
+  }
+  int nc = 0, np = 0;
+  for (int c = t; c < n_leave; c += 256) nc += cflag[c];
+  for (int o = 32; o > 0; o >>= 1) nc += __shfl_xor(nc, o);
+  if ((t & 63) == 0) red[t >> 6] = nc;
+  __syncthreads();
+  const int n_x = n_pool + red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  for (int x = t; x < n_x; x += 256) np += xid[x] < n_sink;
+  for (int o = 32; o > 0; o >>= 1) np += __shfl_xor(np, o);
+  if ((t & 63) == 0) red[t >> 6] = np;
+  __syncthreads();
+  const int n_pin = red[0] + red[1] + red[2] + red[3];
+  if (n_x > C && n_pin > C && t == 0) set_status(status, PBSA_STATUS_SINK);
+  for (int x = t; x < n_x; x += 256) {
+    bool keep;
+    const bool pin = xid[x] < n_sink;
+    if (n_x <= C) {
+      keep = true;
+    } else if (n_pin > C) {  // more sinks than room: the C smallest ids
+      int r = 0;
+      for (int y = 0; y < n_x; ++y) r += (xid[y] < n_sink) && (xid[y] < xid[x]);
+      keep = pin && r < C;
+    } else if (pin) {
+      keep = true;
+    } else {
+      int r = 0;
+      for (int y = 0; y < n_x; ++y)
+        r += (xid[y] >= n_sink) && ranks_before(xm[y], xid[y], xm[x], xid[x]);
+      keep = r < C - n_pin;
+    }
+    xkeep[x] = keep ? 1 : 0;
+  }
+  __syncthreads();
+  // free slots: evicted pool slots and the unused tail, ascending
+  for (int s = t; s < C; s += 256) {
+    const bool fr = s >= n_pool || !xkeep[s];
+    if (!fr) continue;
+    int pos = 0;
+    for (int s2 = 0; s2 < s; ++s2) pos += (s2 >= n_pool || !xkeep[s2]);
+    free_slot[pos] = s;
+  }
+  __syncthreads();
+  int nk = 0, na = 0;
+  for (int x = t; x < n_x; x += 256) {
+    nk += xkeep[x];
+    if (x < n_pool || !xkeep[x]) continue;
+    int pos = 0;  // rank among the admitted by id (ids are unique)
+    for (int y = n_pool; y < n_x; ++y) pos += xkeep[y] && xid[y] < xid[x];
+    const int slot = free_slot[pos];
+    const int w = -1 - xsrc[x];
+    a_slot[bh * C + pos] = slot;
+    a_src[bh * C + pos] = w;
+    pool_len[bh * C + slot] = min(max(win_len[w], 0), T);
+    pool_id[bh * C + slot] = win_id[w];
+    ++na;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    nk += __shfl_xor(nk, o);
+    na += __shfl_xor(na, o);
+  }
+  __syncthreads();
+  if ((t & 63) == 0) red[t >> 6] = nk;
+  __syncthreads();
+  if (t == 0) pool_count[bh] = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  if ((t & 63) == 0) red[t >> 6] = na;
+  __syncthreads();
+  if (t == 0) a_count[bh] = red[0] + red[1] + red[2] + red[3];
+}
+
+// grid (A, H, B): workgroup a copies admitted block a of (b, h) from its
+// window slot into its pool slot (K and V: all T rows; kbar: d floats).
+__global__ __launch_bounds__(256) void update_copy_kernel(
+    const uint8_t *__restrict__ k_win, const uint8_t *__restrict__ v_win,
+    const float *__restrict__ kbar_win, uint8_t *__restrict__ k_pool, uint8_t *__restrict__ v_pool,
+    float *__restrict__ kbar_pool, const int32_t *__restrict__ a_slot,
+    const int32_t *__restrict__ a_src, const int32_t *__restrict__ a_count, int H, int W, int C,
+    int d, size_t block_bytes) {
+  const int a = blockIdx.x;
+  const size_t bh = (size_t)blockIdx.z * H + blockIdx.y;
+  if (a >= a_count[bh]) return;
+  const int slot = a_slot[bh * C + a];
+  const int w = a_src[bh * C + a];
+  const size_t nvec = block_bytes / 16;
+  const u32x4 *ks = reinterpret_cast<const u32x4 *>(k_win + (bh * W + w) * block_bytes);
+  const u32x4 *vs = reinterpret_cast<const u32x4 *>(v_win + (bh * W + w) * block_bytes);
+  u32x4 *kd = reinterpret_cast<u32x4 *>(k_pool + (bh * C + slot) * block_bytes);
+  u32x4 *vd = reinterpret_cast<u32x4 *>(v_pool + (bh * C + slot) * block_bytes);
+  for (size_t e = threadIdx.x; e < nvec; e += 256) {
+    const u32x4 x = ks[e];
+    const u32x4 y = vs[e];
+    kd[e] = x;
+    vd[e] = y;
+  }
+  for (int e = threadIdx.x; e < d; e += 256) kbar_pool[(bh * C + slot) * d + e] = kbar_win[(bh * W + w) * d + e];
+}
+
+size_t update_ws_bytes(const pbsa_problem &p) {
+  const size_t bh = (size_t)p.B * p.H;
+  return 2 * align256(bh * p.C * sizeof(int32_t)) + align256(bh * sizeof(int32_t));
+}
+
+hipError_t launch_memory_update(const pbsa_problem &p, const pbsa_kv &kv, const float *mass_pool,
+                                const float *mass_win, const int32_t *leaving, int n_leave,
+                                int64_t n_sink, void *ws, hipStream_t st) {
+  const size_t bh = (size_t)p.B * p.H;
+  char *w = reinterpret_cast<char *>(ws);
+  int32_t *a_slot = reinterpret_cast<int32_t *>(w);
+  int32_t *a_src = reinterpret_cast<int32_t *>(w + align256(bh * p.C * sizeof(int32_t)));
+  int32_t *a_count = reinterpret_cast<int32_t *>(w + 2 * align256(bh * p.C * sizeof(int32_t)));
+  update_decide_kernel<<<dim3(p.H, p.B), 256, 0, st>>>(
+      mass_pool, mass_win, leaving, n_leave, kv.win_len, kv.win_id, kv.pool_len, kv.pool_id,
+      kv.pool_count, a_slot, a_src, a_count, p.H, p.W, p.C, p.T, n_sink, p.dev_status);
+  const int A = n_leave < p.C ? n_leave : p.C;
+  if (A > 0) {
+    const size_t esz = p.dtype == PBSA_BF16 ? 2 : 4;
+    update_copy_kernel<<<dim3(A, p.H, p.B), 256, 0, st>>>(
+        (const uint8_t *)kv.k_win, (const uint8_t *)kv.v_win, kv.kbar_win, (uint8_t *)kv.k_pool,
+        (uint8_t *)kv.v_pool, kv.kbar_pool, a_slot, a_src, a_count, p.H, p.W, p.C, p.d,
+        (size_t)p.T * p.d * esz);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pbsa

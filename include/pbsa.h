@@ -1,0 +1,220 @@
+/*
+ * pbsa.h - Persistent Block-Sparse Attention (PBSA) for AMD Instinct MI355X
+ * (gfx950), C ABI.
+ *
+ * The method is described on the pages "Sparse Forcing: Native Trainable
+ * Sparse Attention for Real-time Autoregressive Diffusion Video Generation"
+ * (gist.science/es explainer, sec. 2 "Metodologia": "Arquitectura Propuesta"
+ * and "Persistente Block-Sparse Attention (PBSA)"; English abstract on the
+ * shd-paper.top summary page).  Per autoregressive chunk, each query block
+ * attends (1) every block of a small persistent pool P_t, (2) the top-k
+ * blocks of the local sliding window L_t, chosen by coarse routing on
+ * mean-pooled block representatives, and (3) the current chunk itself.
+ * After the chunk, the blocks leaving the window compete with the pool by
+ * pooled attention mass (Top-C retention); sink blocks are pinned.
+ *
+ * Conventions
+ *  - Every pointer is a DEVICE pointer unless stated otherwise.  Tensors are
+ *    dense, row-major, contiguous, head-major (index order as written).
+ *  - "bf16" data is raw bfloat16 bits (uint16); dtype PBSA_F32 uses float.
+ *    Q, K, V, O, dO, dQ, dK, dV share the problem's dtype; pooled means,
+ *    masses and LSE are always fp32; indices int32; block ids int64 (>= 0).
+ *  - The caller owns and allocates every buffer, including the workspace.
+ *    The library allocates nothing, keeps no state between calls and never
+ *    synchronises the host: each call only enqueues kernels on `stream`
+ *    (a hipStream_t; NULL = the null stream).  Calls are thread-safe.
+ *  - Pointers must be 16-byte aligned.
+ *  - Return value: PBSA_OK (0) or a negative PBSA_ERR_* code.  Arguments are
+ *    validated on the host before anything is enqueued; on error nothing is
+ *    launched and outputs are untouched.  pbsa_last_error() gives a
+ *    thread-local detail string.  No C++ exception crosses the ABI.
+ *  - Device-resident metadata (pool_count, win_len, sel) cannot be checked
+ *    on the host without a sync; kernels clamp bad values instead of
+ *    faulting and OR a PBSA_STATUS_* bit into *problem.dev_status (if not
+ *    NULL).
+ *
+ * Shapes (QB = ceil(Nq / T) query blocks; the last block may be short):
+ *   q, k_cur, v_cur, o, dout, dq, dk_cur, dv_cur  [B, H, Nq, d]
+ *   k_win, v_win, dk_win, dv_win                  [B, H, W, T, d]   ring slots
+ *   win_len [W] int32 (0 = empty slot), win_id [W] int64
+ *   k_pool, v_pool, dk_pool, dv_pool              [B, H, C, T, d]
+ *   pool_len [B, H, C] int32, pool_id [B, H, C] int64,
+ *   pool_count [B, H] int32 (valid pool slots are exactly [0, count))
+ *   kbar_win [B, H, W, d], kbar_pool [B, H, C, d], kbar_cur [B, H, QB, d]
+ *   sel [B, H, QB, topk] int32, sel_count [B, H, QB] int32
+ *   mass_pool [B, H, C], mass_win [B, H, W], lse [B, H, Nq]  (fp32)
+ *
+ * Supported: dtype PBSA_BF16 with d in {64, 128} and T in {64, 128}
+ * (bf16 MFMA, fp32 accumulate and softmax); dtype PBSA_F32 with d in
+ * {64, 128}, T in {64, 128} (fp32 vector path).  W <= 1024, C <= 1024,
+ * 0 <= topk <= W.
+ */
+#ifndef PBSA_H
+#define PBSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *pbsa_stream_t; /* hipStream_t */
+
+enum { PBSA_BF16 = 0, PBSA_F32 = 1 };
+
+enum {
+  PBSA_OK = 0,
+  PBSA_ERR_NULL = -1,        /* a required pointer is NULL */
+  PBSA_ERR_SHAPE = -2,       /* a size is out of range */
+  PBSA_ERR_DTYPE = -3,       /* unknown dtype */
+  PBSA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  PBSA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required */
+  PBSA_ERR_HIP = -6,         /* the HIP runtime reported an error */
+  PBSA_ERR_UNSUPPORTED = -7  /* valid but not implemented (e.g. d = 96) */
+};
+
+enum { PBSA_OP_SELECT = 0, PBSA_OP_FWD = 1, PBSA_OP_BWD = 2, PBSA_OP_UPDATE = 3 };
+
+/* Bits OR-ed into *dev_status by kernels (device-side metadata faults). */
+enum {
+  PBSA_STATUS_POOL_COUNT = 1,  /* pool_count outside [0, C]: clamped */
+  PBSA_STATUS_WIN_LEN = 2,     /* a win_len / pool_len outside [0, T]: clamped */
+  PBSA_STATUS_SEL = 4,         /* sel entry outside [0, W) or sel_count > topk: skipped/clamped */
+  PBSA_STATUS_SINK = 8         /* more pinned sink blocks than C: kept the C smallest ids */
+};
+
+typedef struct {
+  int32_t B, H;      /* batch, heads; every (b, h) is independent */
+  int32_t d;         /* head dim */
+  int32_t T;         /* tokens per block (also the query-block height) */
+  int32_t Nq;        /* tokens of the current chunk (>= 1) */
+  int32_t W;         /* window ring slots */
+  int32_t C;         /* pool capacity in blocks */
+  int32_t topk;      /* window blocks selected per query block */
+  int32_t dtype;     /* PBSA_BF16 or PBSA_F32 */
+  float scale;       /* logit scale; 0 means 1/sqrt(d) */
+  int32_t *dev_status; /* optional device int32 for PBSA_STATUS_* bits; may be NULL */
+} pbsa_problem;
+
+/* One layer's KV state; every buffer is caller-owned. */
+typedef struct {
+  const void *k_cur, *v_cur;  /* [B,H,Nq,d] current chunk */
+  const void *k_win, *v_win;  /* [B,H,W,T,d] window ring */
+  const int32_t *win_len;     /* [W] valid tokens per slot, 0 = empty (shared by all b,h) */
+  const int64_t *win_id;      /* [W] global block id of each slot */
+  const float *kbar_win;      /* [B,H,W,d] mean of each window slot's valid keys */
+  void *k_pool, *v_pool;      /* [B,H,C,T,d] persistent pool */
+  int32_t *pool_len;          /* [B,H,C] */
+  int64_t *pool_id;           /* [B,H,C] */
+  int32_t *pool_count;        /* [B,H] */
+  float *kbar_pool;           /* [B,H,C,d] */
+  float *kbar_cur;            /* [B,H,QB,d] written by pbsa_select */
+} pbsa_kv;
+
+/* Gradient buffers, same shapes as the matching pbsa_kv fields. */
+typedef struct {
+  void *dk_cur, *dv_cur, *dk_win, *dv_win, *dk_pool, *dv_pool;
+} pbsa_kv_grad;
+
+/*
+ * pbsa_select - block compression by pooling and coarse routing
+ * (gist.science/es, sec. 2 "Persistente Block-Sparse Attention (PBSA)":
+ * pooled block representatives for coarse routing; "Arquitectura
+ * Propuesta": Top-K window blocks per query, coarse scoring of relevance).
+ *   qbar_i   = mean of the rows of query block i            (fp32)
+ *   kbar_cur = mean of the key rows of each current block   (fp32, written to kv->kbar_cur)
+ *   s_ij     = scale * <qbar_i, kbar_j> for j in the valid pool slots, the
+ *              valid window slots and the current blocks
+ *   sel[i]   = the min(topk, #valid window slots) window slots with the
+ *              largest s_ij (ties: smaller win_id; NaN last), ascending
+ *              slot order, padded with -1; sel_count[i] = their number
+ *   mass_pool / mass_win[j] = sum over query blocks i of softmax_j(s_i.)
+ *              (the softmax runs over pool + window + current); 0 for
+ *              invalid slots.  These are the scores of the Top-C update.
+ * Workspace: pbsa_workspace_size(p, PBSA_OP_SELECT) bytes.
+ */
+int pbsa_select(const pbsa_problem *p, const void *q, const pbsa_kv *kv, int32_t *sel,
+                int32_t *sel_count, float *mass_pool, float *mass_win, void *ws,
+                size_t ws_bytes, pbsa_stream_t stream);
+
+/*
+ * pbsa_attn_fwd - hybrid attention (same section: dense attention over the
+ * persistent memory, sparse attention over the window).  For row r of query
+ * block i, over the tokens U_i = valid tokens of pool slots [0, count),
+ * of the window slots sel[i][0:sel_count[i]], and of the whole current chunk:
+ *   O_r = softmax_u(scale * <Q_r, K_u>) V_u,   lse_r = log sum_u exp(scale <Q_r,K_u>)
+ * (natural log).  o: [B,H,Nq,d] in the problem dtype; lse may be NULL.
+ * Workspace: none required (ws may be NULL).
+ */
+int pbsa_attn_fwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const int32_t *sel,
+                  const int32_t *sel_count, void *o, float *lse, void *ws, size_t ws_bytes,
+                  pbsa_stream_t stream);
+
+/*
+ * pbsa_attn_bwd - gradients through the fixed block mask (the trainable
+ * sparse attention of the paper's title; selection is not differentiated).
+ * With P the forward weights (recomputed from lse), D_r = <dO_r, O_r>,
+ * dS = P (dO V^T - D):  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO,
+ * each landing on the storage slot of its token.  Every element of every
+ * gradient buffer is written (zero where no query attends).  dq and every
+ * pbsa_kv_grad field are required.
+ * Workspace: pbsa_workspace_size(p, PBSA_OP_BWD) bytes.
+ */
+int pbsa_attn_bwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const int32_t *sel,
+                  const int32_t *sel_count, const void *o, const float *lse, const void *dout,
+                  void *dq, const pbsa_kv_grad *g, void *ws, size_t ws_bytes,
+                  pbsa_stream_t stream);
+
+/*
+ * pbsa_memory_update - Top-C retention of the persistent pool ("Arquitectura
+ * Propuesta": sink blocks as fixed anchors, dynamic blocks by coarse score,
+ * Top-C keeps the C best and discards the rest of the blocks leaving the
+ * window).  Per (b, h): candidates X = valid pool blocks + the window slots
+ * listed in `leaving` (device int32 [n_leave], slots with win_len 0 and ids
+ * already in the pool are skipped).  If |X| <= C all are kept; otherwise the
+ * blocks with id < n_sink are pinned and the rest ranked by mass (desc, then
+ * id asc, NaN last).  Survivors keep their slots; admitted blocks fill the
+ * freed slots, then the unused tail, in ascending slot order and ascending
+ * id order, copying K, V (all T rows), kbar, len and id bit-exactly.
+ * pool_count becomes |kept|.  Reads kv->k_win/v_win/kbar_win/win_*.
+ * Workspace: pbsa_workspace_size(p, PBSA_OP_UPDATE) bytes.  n_leave <= W.
+ */
+int pbsa_memory_update(const pbsa_problem *p, const pbsa_kv *kv, const float *mass_pool,
+                       const float *mass_win, const int32_t *leaving, int32_t n_leave,
+                       int64_t n_sink, void *ws, size_t ws_bytes, pbsa_stream_t stream);
+
+/*
+ * pbsa_block_mean - pooled representative (mean of the valid rows) of
+ * n_blocks stored blocks: x [n_blocks, T, d] in the problem dtype, len
+ * [n_blocks] int32 (or NULL = all T), out [n_blocks, d] fp32.  Blocks with
+ * len 0 get 0.  Used to fill kbar caches for a state built outside a
+ * rollout (same pooling as pbsa_select).
+ */
+int pbsa_block_mean(const pbsa_problem *p, const void *x, const int32_t *len, int64_t n_blocks,
+                    float *out, pbsa_stream_t stream);
+
+/*
+ * pbsa_window_append - the ring advance of a rollout: write the current
+ * chunk (k_cur/v_cur of kv, kbar_cur) into QB consecutive window slots
+ * [first_slot, first_slot + QB) and set their win_len (block length) and
+ * win_id (first_id + j).  win_len/win_id are passed writable here.
+ */
+int pbsa_window_append(const pbsa_problem *p, const pbsa_kv *kv, void *k_win, void *v_win,
+                       float *kbar_win, int32_t *win_len, int64_t *win_id, int32_t first_slot,
+                       int64_t first_id, pbsa_stream_t stream);
+
+/* Bytes of workspace an op needs (0 if none). */
+size_t pbsa_workspace_size(const pbsa_problem *p, int op);
+
+/* Host-only validation of the problem for an op (same checks the entry
+ * points run first).  Returns PBSA_OK or a PBSA_ERR_* code. */
+int pbsa_validate(const pbsa_problem *p, int op);
+
+const char *pbsa_strerror(int status);
+const char *pbsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PBSA_H */

@@ -40,7 +40,8 @@ each reading is tagged R<n> and listed with its basis in the design notes:
   R11 block mass = coarse softmax over everything the chunk can see, summed
       over the chunk's query blocks
   R12 update candidates = valid pool blocks + blocks leaving the window
-      (a leaving block whose id is already pooled is not a second candidate)
+      (a leaving block whose id is already pooled, or listed earlier among
+      the leaving blocks, is not a second candidate)
   R13 Top-C order: mass descending, then id ascending; NaN last; blocks with
       id < n_sink are pinned (sinks)
   R14 a block enters the pool as a bit-exact copy of its K/V/mean/len/id
@@ -352,11 +353,12 @@ def memory_update_one(pool_ids: list, pool_mass: list, cand_ids: list, cand_mass
     STATUS_SINK_OVERFLOW.
     """
     n_pool = len(pool_ids)
-    pooled = set(int(x) for x in pool_ids)
+    seen = set(int(x) for x in pool_ids)
     X = [("pool", p, int(pool_ids[p]), float(pool_mass[p])) for p in range(n_pool)]
     for c in range(len(cand_ids)):
-        if int(cand_ids[c]) in pooled:                       # R12: already resident
+        if int(cand_ids[c]) in seen:       # R12: already resident or already listed
             continue
+        seen.add(int(cand_ids[c]))
         X.append(("cand", c, int(cand_ids[c]), float(cand_mass[c])))
     status = 0
     if len(X) <= C:

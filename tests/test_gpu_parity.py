@@ -1,0 +1,255 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars (from the method's target numerics: bf16 inputs, fp32 accumulation):
+  - selected window blocks: identical sets, except inside the tie band where
+    the k-th and (k+1)-th coarse logits differ by <= 1e-4 relative (there
+    any choice within the band is accepted and checked for validity);
+  - block masses: fp32 vs fp64, rtol 1e-4;
+  - attention outputs: max-abs <= 2e-2 AND max-abs / max|O_oracle| <= 2e-2
+    on the bf16 path; <= 1e-4 max-abs on the fp32 path;
+  - LSE: max-abs <= 2e-3 (bf16), 1e-5 (fp32);
+  - memory update: pool membership, slot placement and copied bytes exact
+    (teacher-forced on the GPU's own masses, so routing noise cannot cascade).
+Attention and update are checked on the GPU's own selection (teacher forcing).
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import pbsa_synth as syn
+from oracle import pbsa_oracle as po
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from block_sparse_attention_20_amd.layer import PBSALayer
+    from block_sparse_attention_20_amd import pbsa as P
+
+TIE_REL = 1e-4
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run(shape, st, scale=0.0, device="cuda"):
+    L = PBSALayer(shape.B, shape.H, shape.d, shape.T, shape.Nq, shape.W, shape.C, shape.topk,
+                  dtype=shape.dtype, scale=scale, device=device).load(st)
+    L.select()
+    L.fwd()
+    torch.cuda.synchronize()
+    return L
+
+
+def eff_scale(shape, scale):
+    return scale if scale > 0 else 1.0 / math.sqrt(shape.d)
+
+
+def check_selection(L, r, st, k):
+    gsel = L.t["sel"].cpu().numpy()[..., :max(k, 1)]
+    gcnt = L.t["sel_count"].cpu().numpy()
+    np.testing.assert_array_equal(gcnt, r["sel_count"])
+    win_id = np.asarray(st["win_id"])
+    n_tie = 0
+    for idx in np.ndindex(*gcnt.shape):
+        g = [int(w) for w in gsel[idx][:gcnt[idx]]]
+        o = [int(w) for w in r["sel"][idx][:r["sel_count"][idx]]]
+        assert g == sorted(g), "selection must be in ascending slot order"
+        assert all(w == -1 for w in gsel[idx][gcnt[idx]:k]), "padding must be -1"
+        if g == o:
+            continue
+        # tie band: every slot in the symmetric difference scores within 1e-4
+        # relative of the oracle's k-th score
+        s = r["s_win"][idx]
+        valid = [w for w in range(len(s)) if not np.isnan(s[w])]
+        order = sorted(valid, key=lambda w: po.rank_key_desc(s[w], int(win_id[w])))
+        kth = s[order[k - 1]]
+        for w in set(g) ^ set(o):
+            assert abs(s[w] - kth) <= TIE_REL * max(abs(s[w]), abs(kth)), (idx, w, s[w], kth)
+        n_tie += 1
+    return n_tie
+
+
+def check_close_bf16(got, ref, what):
+    ref = np.asarray(ref)
+    m = ~np.isnan(ref)
+    err = np.abs(got[m] - ref[m]).max()
+    scale = np.abs(ref[m]).max()
+    _log(f"{what}: max-abs {err:.3e}, normalised {err / scale:.3e}")
+    assert err <= 2e-2, (what, err)
+    assert err / scale <= 2e-2, (what, err / scale)
+    return err
+
+
+# ------------------------------------------------------------------- cases ---
+CASES = {
+    # ragged tail query block, empty + ragged window slots, pools of 3 and 1
+    "bf16_d128_T128_small": (syn.Shape(B=1, H=2, d=128, T=128, Nq=3 * 128 - 40, W=6, C=3, topk=2),
+                             dict(sigma=1.0, shift=1.0, n_planted=2, win_len=[128, 128, 88, 128, 0, 128],
+                                  pool_count=[3, 1], pool_len=[128, 60, 128, 128, 128, 128])),
+    # several tiles, d=64/T=64, batch 2, unscaled N(0,1)
+    "bf16_d64_T64_multi": (syn.Shape(B=2, H=2, d=64, T=64, Nq=5 * 64 - 7, W=10, C=4, topk=3),
+                           dict(sigma=1.0, shift=1.5, n_planted=3, win_len=[64] * 4 + [33] + [64] * 4 + [1],
+                                pool_count=[4, 2, 0, 3])),
+    "bf16_d64_T128": (syn.Shape(B=1, H=2, d=64, T=128, Nq=2 * 128 + 5, W=4, C=2, topk=2),
+                      dict(sigma=1.0, n_planted=0, win_len=[128, 5, 128, 128], pool_count=[2, 1])),
+    "bf16_d128_T64": (syn.Shape(B=1, H=1, d=128, T=64, Nq=4 * 64, W=8, C=4, topk=8),
+                      dict(sigma=1.0, n_planted=2, shift=1.0, pool_count=4)),
+    "f32_d64_T64": (syn.Shape(B=1, H=2, d=64, T=64, Nq=3 * 64 - 9, W=5, C=2, topk=2, dtype=torch.float32),
+                    dict(sigma=1.0, n_planted=1, shift=1.0, win_len=[64, 64, 20, 64, 64], pool_count=[2, 1])),
+    "f32_d128_T128": (syn.Shape(B=1, H=1, d=128, T=128, Nq=200, W=3, C=2, topk=1, dtype=torch.float32),
+                      dict(sigma=1.0, pool_count=2)),
+    # degenerate: no pool, no window blocks valid, single ragged query block
+    "empty_pool_and_window": (syn.Shape(B=1, H=2, d=128, T=128, Nq=77, W=3, C=2, topk=2),
+                              dict(sigma=1.0, win_len=[0, 0, 0], pool_count=0)),
+    # k >= valid window slots: everything selected
+    "topk_covers_window": (syn.Shape(B=1, H=1, d=128, T=128, Nq=256, W=4, C=1, topk=4),
+                           dict(sigma=1.0, win_len=[128, 0, 128, 64], pool_count=1)),
+    # W = 0, C = 0: the current chunk only
+    "current_only": (syn.Shape(B=1, H=3, d=64, T=64, Nq=130, W=0, C=0, topk=0),
+                     dict(sigma=1.0, win_len=[], pool_count=0)),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_select_and_fwd_match_oracle(name):
+    shape, kw = CASES[name]
+    _log(f"case {name}")
+    st = syn.make_state(shape, 11, pad_value=float("nan"), **kw)
+    L = run(shape, st)
+    scale = eff_scale(shape, 0.0)
+    r = po.select(st, shape.topk, scale, shape.T)
+    if shape.topk > 0:
+        check_selection(L, r, st, shape.topk)
+    else:
+        assert (L.t["sel_count"] == 0).all()
+    # masses (fp32 vs fp64)
+    if shape.C > 0:
+        np.testing.assert_allclose(L.t["mass_pool"].cpu().numpy(), r["mass_pool"], rtol=1e-4, atol=1e-6)
+    if shape.W > 0:
+        np.testing.assert_allclose(L.t["mass_win"].cpu().numpy(), r["mass_win"], rtol=1e-4, atol=1e-6)
+    np.testing.assert_allclose(L.t["kbar_cur"].cpu().numpy(), r["kbar_cur"], rtol=1e-5, atol=1e-5)
+    # attention on the GPU's own selection
+    gsel = L.t["sel"].cpu().numpy(); gcnt = L.t["sel_count"].cpu().numpy()
+    f = po.attn_fwd(st, gsel, gcnt, scale, shape.T)
+    o = L.t["o"].float().cpu().numpy()
+    lse = L.t["lse"].cpu().numpy()
+    if shape.dtype == torch.float32:
+        assert np.abs(o - f["o"]).max() <= 1e-4
+        assert np.abs(lse - f["lse"]).max() <= 1e-5
+    else:
+        check_close_bf16(o, f["o"], name)
+        assert np.abs(lse - f["lse"]).max() <= 2e-3
+    assert not np.isnan(o).any(), "padding rows leaked NaN into the output"
+    assert L.status_bits() == 0
+
+
+def test_fwd_deterministic_and_fully_written():
+    shape, kw = CASES["bf16_d64_T64_multi"]
+    st = syn.make_state(shape, 3, **kw)
+    L = run(shape, st)
+    o1 = L.t["o"].clone(); l1 = L.t["lse"].clone()
+    L.t["o"].fill_(float("nan")); L.t["lse"].fill_(float("nan"))
+    L.fwd()
+    torch.cuda.synchronize()
+    assert torch.equal(L.t["o"], o1) and torch.equal(L.t["lse"], l1)
+
+
+def test_memory_update_matches_oracle():
+    shape = syn.Shape(B=1, H=3, d=128, T=128, Nq=300, W=8, C=5, topk=3)
+    st = syn.make_state(shape, 5, sigma=1.0, shift=1.0, n_planted=3,
+                        win_len=[128, 128, 44, 128, 0, 128, 128, 17], pool_count=[5, 2, 0],
+                        pool_len=[128, 128, 100, 128, 128] * 3, pool_id=list(range(5)) * 3,
+                        win_id=list(range(10, 18)))
+    L = run(shape, st)
+    before = {k: L.t[k].clone() for k in ("k_pool", "v_pool", "kbar_pool", "pool_id", "pool_len")}
+    leaving = [0, 1, 2, 3, 4, 7, 2]  # slot 4 empty, slot 2 listed twice
+    mp = L.t["mass_pool"].cpu().numpy(); mw = L.t["mass_win"].cpu().numpy()
+    kbw = L.t["kbar_win"].cpu().numpy(); kbp = L.t["kbar_pool"].cpu().numpy()
+    L.update(torch.tensor(leaving, dtype=torch.int32, device="cuda"), n_sink=1)
+    torch.cuda.synchronize()
+    u = po.memory_update(st, mp, mw, leaving, 1, kbar_win=kbw, kbar_pool=kbp)
+    np.testing.assert_array_equal(L.t["pool_count"].cpu().numpy(), u["pool_count"])
+    cnt = u["pool_count"]
+    for b, h in np.ndindex(shape.B, shape.H):
+        n = cnt[b, h]
+        np.testing.assert_array_equal(L.t["pool_id"][b, h, :n].cpu().numpy(), u["pool_id"][b, h, :n])
+        np.testing.assert_array_equal(L.t["pool_len"][b, h, :n].cpu().numpy(), u["pool_len"][b, h, :n])
+        np.testing.assert_array_equal(L.t["kbar_pool"][b, h, :n].cpu().numpy(), u["kbar_pool"][b, h, :n])
+        # copied K/V are bit-exact copies of their window slot; survivors untouched
+        for slot, w in u["admitted"][(b, h)]:
+            assert torch.equal(L.t["k_pool"][b, h, slot], L.t["k_win"][b, h, w])
+            assert torch.equal(L.t["v_pool"][b, h, slot], L.t["v_win"][b, h, w])
+        admitted = {s for s, _ in u["admitted"][(b, h)]}
+        for slot in range(shape.C):
+            if slot not in admitted:
+                assert torch.equal(L.t["k_pool"][b, h, slot], before["k_pool"][b, h, slot])
+    assert L.status_bits() == 0
+
+
+def test_window_append_copies_chunk():
+    shape = syn.Shape(B=1, H=2, d=64, T=64, Nq=150, W=6, C=1, topk=1)
+    st = syn.make_state(shape, 2, win_len=[64, 64, 22, 0, 0, 0], pool_count=1)
+    L = run(shape, st)
+    L.append_window(3, 1000)
+    torch.cuda.synchronize()
+    assert L.t["win_len"].cpu().tolist() == [64, 64, 22, 64, 64, 22]
+    assert L.t["win_id"].cpu().tolist()[3:] == [1000, 1001, 1002]
+    for j, n in enumerate([64, 64, 22]):
+        assert torch.equal(L.t["k_win"][:, :, 3 + j, :n], L.t["k_cur"][:, :, 64 * j:64 * j + n])
+        assert torch.equal(L.t["v_win"][:, :, 3 + j, :n], L.t["v_cur"][:, :, 64 * j:64 * j + n])
+        assert torch.equal(L.t["kbar_win"][:, :, 3 + j], L.t["kbar_cur"][:, :, j])
+
+
+def test_bad_device_metadata_is_clamped_and_flagged():
+    shape = syn.Shape(B=1, H=1, d=64, T=64, Nq=64, W=3, C=2, topk=2)
+    st = syn.make_state(shape, 1, pool_count=2)
+    L = run(shape, st)
+    o_ref = L.t["o"].clone()
+    L.t["pool_count"].fill_(99)        # > C: clamped to C
+    L.t["sel"][0, 0, 0, 1] = 1000      # outside [0, W): skipped
+    L.fwd()
+    torch.cuda.synchronize()
+    bits = L.status_bits()
+    assert bits & P.PBSA_STATUS_POOL_COUNT and bits & P.PBSA_STATUS_SEL
+    assert not torch.isnan(L.t["o"].float()).any()
+    del o_ref
+
+
+# ------------------------------------------------------- Wan-shaped chunk ---
+@pytest.mark.parametrize("unscaled", [False, True])
+def test_wan_chunk_full_size(unscaled):
+    """The Wan2.1-1.3B-shaped chunk (12 heads, 4680 tokens, window 74, pool 32,
+    top-16) at full size, in the launch configuration the benchmark times:
+    full selection and masses against the oracle; attention on sampled query
+    blocks (first, middle, the ragged tail) of several heads."""
+    _log(f"wan chunk unscaled={unscaled}")
+    shape = syn.WAN_CHUNK
+    st = syn.wan_chunk_state(0, unscaled=unscaled)
+    L = run(shape, st)
+    scale = 1 / math.sqrt(128)
+    r = po.select(st, shape.topk, scale, shape.T)
+    n_tie = check_selection(L, r, st, shape.topk)
+    _log(f"tie-band rows: {n_tie}")
+    # planted blocks are recalled by every query block
+    gsel = L.t["sel"].cpu().numpy(); gcnt = L.t["sel_count"].cpu().numpy()
+    for idx in np.ndindex(*gcnt.shape):
+        assert set(st["planted"]) <= set(gsel[idx].tolist())
+    np.testing.assert_allclose(L.t["mass_pool"].cpu().numpy(), r["mass_pool"], rtol=1e-4, atol=1e-6)
+    np.testing.assert_allclose(L.t["mass_win"].cpu().numpy(), r["mass_win"], rtol=1e-4, atol=1e-6)
+    blocks = [(0, h, i) for h in (0, 5, 11) for i in (0, 17, 36)]
+    f = po.attn_fwd(st, gsel, gcnt, scale, shape.T, blocks=blocks)
+    o = L.t["o"].float().cpu().numpy()
+    rows = np.concatenate([np.arange(i * 128, min(4680, i * 128 + 128)) for _, _, i in blocks[:3]])
+    got = np.concatenate([o[0, h, rows] for h in (0, 5, 11)])
+    ref = np.concatenate([f["o"][0, h, rows] for h in (0, 5, 11)])
+    check_close_bf16(got, ref, f"wan chunk (unscaled={unscaled})")
+    lse = L.t["lse"].cpu().numpy()
+    lref = np.concatenate([f["lse"][0, h, rows] for h in (0, 5, 11)])
+    lgot = np.concatenate([lse[0, h, rows] for h in (0, 5, 11)])
+    assert np.abs(lgot - lref).max() <= 2e-3

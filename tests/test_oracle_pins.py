@@ -402,6 +402,12 @@ def test_update_small_pool_keeps_everything_and_fills_tail():
     assert new_ids == [5, 9, 20, 30] and assign == [(2, 1), (3, 0)] and st == 0
 
 
+def test_update_duplicate_leaving_ids_count_once():
+    # the same block listed twice among the leaving blocks is one candidate
+    assign, new_ids, _ = po.memory_update_one([1], [0.1], [5, 5, 6], [0.9, 0.9, 0.2], 3, 0)
+    assert new_ids == [1, 5, 6] and assign == [(1, 0), (2, 2)]
+
+
 def test_update_ties_and_nan():
     # equal mass: smaller id wins; NaN mass ranks last
     assign, new_ids, _ = po.memory_update_one([7, 3], [0.5, float("nan")], [4, 8], [0.5, 0.5], 2, 0)
