@@ -7,19 +7,25 @@
 // local window).  Query block i attends every valid pool slot, its selected
 // window slots and the whole current chunk; softmax over all of them.
 //
-// bf16 path (gfx950 MFMA), one workgroup per (b, h, query block):
+// bf16 path (gfx950 MFMA), one workgroup per (b, h, query block), two
+// workgroups per CU (64 KB LDS and <= 256 VGPRs each):
 //   - T/32 waves, wave w owns query rows [32w, 32w+32) of the block;
 //   - the block list (pool, selected window slots, current chunk) is walked
-//     in order; each T-token K/V block is staged in LDS (double buffered,
-//     the next block's global loads are in flight while the current one is
-//     computed); padding rows are zero-filled so they cannot inject NaN;
+//     in order.  K and V of a block are moved HBM -> LDS by
+//     global_load_lds_dwordx4 (no register round trip) into row-major tiles
+//     whose 16-byte chunks are XOR-swizzled per row; rows past the valid
+//     length come from a zero page, so padding can never inject NaN;
+//   - the next block's K is in flight while the softmax and P V of the
+//     current block run, and its V while the next S is computed (one K and
+//     one V buffer, four barriers per block);
 //   - S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q held
 //     in registers for the whole kernel), so each lane owns one query column
-//     and the row softmax is mostly in-lane (one cross-half exchange);
-//   - online softmax in the log2 domain, P rounded to bf16 and fed straight
-//     from the accumulator registers as the B operand of O^T = V^T P^T;
-//     V is transposed while it is staged (register 4x4-token transpose)
-//     into a token-permuted layout so each A fragment is one 16-byte read.
+//     and the row softmax is in-lane plus one cross-half exchange;
+//   - online softmax in the log2 domain; the running max only moves when a
+//     block raises it by more than 8 (P <= 2^8), so O is rarely rescaled;
+//   - P is rounded to bf16 in registers and is directly the B operand of
+//     O^T = V^T P^T; the V^T A operand is read from the row-major V tile with
+//     ds_read_b64_tr_b16 (two 4x16 transposed reads per fragment);
 //   - work items are mapped XCD-aware: consecutive query blocks of a head
 //     run on the same XCD and share its L2 for the pool/current K/V.
 // fp32 path: plain vector FMA version of the same walk (small problems).
@@ -96,21 +102,61 @@ __device__ __forceinline__ int clamp_counts(const FwdArgs &a, size_t bh, int i, 
   return n_pool + sc + a.QB;
 }
 
-// swap bits 0 and 1: position of a 4-token group in the permuted V^T layout
-__device__ __forceinline__ int perm4(int rg) { return (rg & ~3) | ((rg & 1) << 1) | ((rg >> 1) & 1); }
+// 256 bytes of zeros: the DMA source for rows past a block's valid length
+// (padding rows and the tail of the last current block), so that they land
+// in LDS as zeros without a register round trip.
+__device__ __attribute__((aligned(256))) uint32_t g_zero_rows[64];
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// s_waitcnt immediate: vmcnt <= n, expcnt and lgkmcnt unconstrained (gfx9 encoding)
+#define PBSA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14)))
+
+// Stage one [BT][D] bf16 block (rows >= len read as zeros) into LDS with the
+// 16-byte chunks of each row XOR-permuted by a row-dependent swizzle (K:
+// row & 7; V: 2 (row & 7), or 2 (row & 3) when a row has 8 chunks).  Each
+// wave moves IPW chunks of 1 KB with global_load_lds_dwordx4 (lane l lands
+// at base + 16 l), so the whole block is in flight without touching VGPRs.
+// Every wave's first row is a multiple of 8, so the swizzle depends only on
+// the lane and the instruction index.
+template <int D, int BT, int NW, bool VSWZ>
+__device__ __forceinline__ void dma_block(uint16_t *lds, const uint16_t *src, int len, int wave,
+                                          int lane) {
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;         // rows per 1 KB instruction
+  constexpr int IPW = BT * D * 2 / 1024 / NW;
+  static_assert((IPW * RPI) % 8 == 0, "wave row ranges must start at multiples of 8");
+  const int p = lane % CPR, rsub = lane / CPR;
+  const int row0 = wave * IPW * RPI;
+  uint16_t *dst = lds + wave * IPW * 512;
+  if (len >= BT) {
+#pragma unroll
+    for (int it = 0; it < IPW; ++it) {
+      const int rl = it * RPI + rsub;  // row - row0
+      const int sw = VSWZ ? (CPR == 16 ? 2 * (rl & 7) : 2 * (rl & 3)) : (rl & 7);
+      __builtin_amdgcn_global_load_lds(src + (size_t)(row0 + rl) * D + (p ^ sw) * 8,
+                                       (lds_void *)(dst + it * 512), 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < IPW; ++it) {
+      const int rl = it * RPI + rsub;
+      const int sw = VSWZ ? (CPR == 16 ? 2 * (rl & 7) : 2 * (rl & 3)) : (rl & 7);
+      const void *g = row0 + rl < len ? (const void *)(src + (size_t)(row0 + rl) * D + (p ^ sw) * 8)
+                                      : (const void *)(g_zero_rows + p * 4);
+      __builtin_amdgcn_global_load_lds(g, (lds_void *)(dst + it * 512), 16, 0, 0);
+    }
+  }
+}
 
 template <int D, int BT>
-__global__ __launch_bounds__(2 * BT) void attn_fwd_bf16_kernel(FwdArgs a) {
-  constexpr int NT = 2 * BT;       // threads: BT/32 waves of 64
-  constexpr int KS = D + 8;        // padded K row (bf16 elements)
-  constexpr int VS = BT + 8;       // padded V^T row
-  constexpr int KCH = BT * D / 8;  // 16-byte chunks per K block
-  constexpr int KIT = KCH / NT;
-  constexpr int VUN = (BT / 4) * (D / 8);  // V units of 4 tokens x 8 dims
-  constexpr int VIT = VUN / NT;
-  static_assert(KCH % NT == 0 && VUN % NT == 0, "tile sizes");
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BT * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VS];
+__global__ __launch_bounds__(2 * BT, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
+  constexpr int NW = BT / 32;               // waves; wave w owns query rows [32w, 32w+32)
+  constexpr int CPR = D / 8;
+  constexpr int IPW = BT * D * 2 / 1024 / NW;
+  __shared__ __attribute__((aligned(1024))) uint16_t Kl[BT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vl[BT * D];
 
   int item;
   item_of_block(a, item);
@@ -118,7 +164,8 @@ __global__ __launch_bounds__(2 * BT) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int i = item % a.QB;
   const size_t bh = item / a.QB;
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   int n_pool, sc;
   const int nb = clamp_counts(a, bh, i, n_pool, sc);
@@ -127,7 +174,7 @@ __global__ __launch_bounds__(2 * BT) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int qrow = i * BT + wave * 32 + l32;
   bf16x8 qf[D / 16];
   {
-    const uint16_t *qp = (const uint16_t *)a.q + (bh * a.Nq + qrow) * (size_t)D;
+    const uint16_t *qp = (const uint16_t *)a.q + (bh * a.Nq + (qrow < a.Nq ? qrow : 0)) * (size_t)D;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       u32x4 v = {0, 0, 0, 0};
@@ -135,98 +182,64 @@ __global__ __launch_bounds__(2 * BT) void attn_fwd_bf16_kernel(FwdArgs a) {
       qf[kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
-
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
   float m = -INFINITY, l = 0.f;
+  const float sl2 = a.sl2;
 
-  u32x4 kreg[KIT];
-  u32x4 vreg[VIT][4];
-  int len_next = 0;
+  // Per-lane LDS element offsets, fixed for the whole kernel (the swizzle of
+  // a row depends only on row & 7, which is fixed by the lane).
+  // K fragment (A of S^T): row tt*32 + l32, logical chunk 2kk + g.
+  int koff[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = l32 * D + (((2 * kk + g) ^ (l32 & 7)) * 8);
+  // V^T fragment via ds_read_b64_tr_b16: in each 16-lane group, lane gi
+  // addresses row gi/4 of a 4-row band (rows tt*32 + 16h + 4g + gi/4, and the
+  // band 8 rows further) and 4 of the group's 16 dims; it receives dim gi of
+  // the 4 rows.
+  const int gi = lane & 15, q16 = (lane >> 4) & 1;
+  const int vr = gi >> 2, vq = gi & 3;
+  const int vsw = CPR == 16 ? 2 * ((4 * g + vr) & 7) : 2 * ((4 * g + vr) & 3);
+  int voff[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+    voff[dt] = (4 * g + vr) * D + (((4 * dt + 2 * q16 + (vq >> 1)) ^ vsw) * 8) + (vq & 1) * 4;
 
-  auto load_block = [&](int j) {
-    const uint16_t *kp, *vp;
-    int len;
-    resolve_block<uint16_t, D, BT>(a, bh, i, n_pool, sc, j, kp, vp, len);
-    len_next = len;
-#pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int c = t + it * NT;
-      const int row = c / (D / 8), col = c % (D / 8);
-      u32x4 v = {0, 0, 0, 0};
-      if (row < len) v = *reinterpret_cast<const u32x4 *>(kp + row * D + col * 8);
-      kreg[it] = v;
-    }
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int u = t + it * NT;
-      const int rg = u % (BT / 4), dg = u / (BT / 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = rg * 4 + e;
-        u32x4 v = {0, 0, 0, 0};
-        if (row < len) v = *reinterpret_cast<const u32x4 *>(vp + row * D + dg * 8);
-        vreg[it][e] = v;
-      }
-    }
-  };
-  auto store_block = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int c = t + it * NT;
-      const int row = c / (D / 8), col = c % (D / 8);
-      *reinterpret_cast<u32x4 *>(&Ks[buf][row * KS + col * 8]) = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int u = t + it * NT;
-      const int rg = u % (BT / 4), dg = u / (BT / 4);
-      uint16_t *dst = &Vt[buf][(dg * 8) * VS + perm4(rg) * 4];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int wd = c >> 1;
-        u32x2 pk;
-        if (c & 1) {
-          pk[0] = (vreg[it][0][wd] >> 16) | (vreg[it][1][wd] & 0xffff0000u);
-          pk[1] = (vreg[it][2][wd] >> 16) | (vreg[it][3][wd] & 0xffff0000u);
-        } else {
-          pk[0] = (vreg[it][0][wd] & 0xffffu) | (vreg[it][1][wd] << 16);
-          pk[1] = (vreg[it][2][wd] & 0xffffu) | (vreg[it][3][wd] << 16);
-        }
-        *reinterpret_cast<u32x2 *>(dst + c * VS) = pk;
-      }
-    }
-  };
-
-  load_block(0);
-  int len_cur = len_next;
-  store_block(0);
+  const uint16_t *kp, *vp;
+  int len;
+  resolve_block<uint16_t, D, BT>(a, bh, i, n_pool, sc, 0, kp, vp, len);
+  dma_block<D, BT, NW, false>(Kl, kp, len, wave, lane);
+  dma_block<D, BT, NW, true>(Vl, vp, len, wave, lane);
+  PBSA_WAIT_VM(0);
   __syncthreads();
 
-  const float sl2 = a.sl2;
   for (int j = 0; j < nb; ++j) {
-    const int cur = j & 1;
-    if (j + 1 < nb) load_block(j + 1);
-
-    // S^T[token][query] = K Q^T
+    const int len_cur = len;
+    // ---- S^T[token][query] = K Q^T
     f32x16 sacc[BT / 32];
 #pragma unroll
     for (int tt = 0; tt < BT / 32; ++tt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[tt][e] = 0.f;
-    const uint16_t *kb = &Ks[cur][l32 * KS + g * 8];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
 #pragma unroll
       for (int tt = 0; tt < BT / 32; ++tt) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kb + tt * 32 * KS + kk * 16);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&Kl[tt * 32 * D + koff[kk]]);
         sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc[tt], 0, 0, 0);
       }
     }
-    // mask padding tokens, row max
+    __syncthreads();  // every wave is done with K
+    const bool more = j + 1 < nb;
+    if (more) {
+      resolve_block<uint16_t, D, BT>(a, bh, i, n_pool, sc, j + 1, kp, vp, len);
+      dma_block<D, BT, NW, false>(Kl, kp, len, wave, lane);
+    }
+    // ---- online softmax (log2 domain); the running max only moves when a
+    // block raises it by more than 8, so O is rarely rescaled and P <= 2^8.
     if (len_cur < BT) {
 #pragma unroll
       for (int tt = 0; tt < BT / 32; ++tt)
@@ -241,19 +254,22 @@ __global__ __launch_bounds__(2 * BT) void attn_fwd_bf16_kernel(FwdArgs a) {
     for (int tt = 0; tt < BT / 32; ++tt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[tt][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx * sl2);
-    const float muse = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(m - muse);
-    m = mnew;
-    l *= alpha;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    if (__ballot(mx > m + 8.f)) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // m = -inf -> 0
+      m = mnew;
+      l *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
-
-    // O^T += V^T P^T
-    const uint16_t *vb = &Vt[cur][l32 * VS + g * 8];
+        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+    }
+    const float muse = m == -INFINITY ? 0.f : m;
+    if (!more) PBSA_WAIT_VM(0);
+    else PBSA_WAIT_VM(IPW);  // V of this block has landed (K of the next may be in flight)
+    __syncthreads();
+    // ---- O^T += V^T P^T
 #pragma unroll
     for (int tt = 0; tt < BT / 32; ++tt) {
 #pragma unroll
@@ -267,16 +283,22 @@ __global__ __launch_bounds__(2 * BT) void attn_fwd_bf16_kernel(FwdArgs a) {
         }
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const bf16x8 va = *reinterpret_cast<const bf16x8 *>(vb + dt * 32 * VS + tt * 32 + h * 16);
+          const int r1 = (tt * 32 + 16 * h) * D + voff[dt];
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&Vl[r1]));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&Vl[r1 + 8 * D]));
+          const bf16x8 va = __builtin_bit_cast(
+              bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){
+                          lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf, oacc[dt], 0, 0, 0);
         }
       }
     }
-    if (j + 1 < nb) {
-      store_block(cur ^ 1);
-      len_cur = len_next;
+    if (more) {
+      __syncthreads();  // every wave is done with V
+      dma_block<D, BT, NW, true>(Vl, vp, len, wave, lane);
+      PBSA_WAIT_VM(IPW);  // the next K has landed
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // epilogue: O = O^T / l, LSE = ln(sum exp(scale s))
