@@ -5,9 +5,11 @@ Workload (one step = one chunk of a streaming rollout in steady state):
 the Wan2.1-T2V-1.3B-shaped chunk - 30 layers, each with 12 heads of 128, a
 4680-token chunk (37 blocks of 128, the last 72 tokens), a window of the two
 previous chunks (74 slots), a full persistent pool of 32 blocks and top-16
-window selection.  Per layer: pbsa_select -> pbsa_attn_fwd ->
-pbsa_memory_update (the 37 blocks of chunk t-2 leave the window) ->
-pbsa_window_append (chunk t takes their slots).  Inputs are synthetic
+window selection.  Per layer: pbsa_select -> pbsa_attn_fwd on the
+critical path, then pbsa_memory_update (the 37 blocks of chunk t-2 leave
+the window) -> pbsa_window_append (chunk t takes their slots) on a side
+stream: the next layer needs only the attention output, the updated cache is
+needed by the next chunk.  Inputs are synthetic
 (seeded, generated on the device) and resident in HBM before timing.
 
 Prints ONE JSON line: attention TFLOP/s over the whole step (algorithmic
@@ -31,6 +33,26 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 
+# HBM traffic of one forward launch on this workload, from two rocprofv3
+# --pmc passes (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by
+# what the same counter reads for a copy kernel of known size (the window
+# append: 28,302 KiB read and 28,302 KiB written per launch; it reads back
+# FETCH 14,166 KiB, WRITE 28,304 KiB).  Valid only for the kernel source it
+# was measured on (sha1 below); reported as null once that source changes.
+FWD_TRAFFIC = {"src_sha1": "373cc33055a158ee7e5156a3df8bfa3b37180dd6",
+               "fetch_kib": 59748.0, "write_kib": 14259.55,
+               "fetch_scale": 28302.0 / 14166.05, "write_scale": 28302.0 / 28304.32}
+
+
+def fwd_traffic_bytes():
+    import hashlib
+    src = os.path.join(ROOT, "block_sparse_attention_20_amd", "csrc", "pbsa_attn_fwd.hip")
+    with open(src, "rb") as f:
+        if hashlib.sha1(f.read()).hexdigest() != FWD_TRAFFIC["src_sha1"]:
+            return None
+    t = FWD_TRAFFIC
+    return round(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]))
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -40,7 +62,8 @@ def build_rollout(n_layers, device):
     import pbsa_synth as syn
     from block_sparse_attention_20_amd.rollout import Rollout
     s = syn.WAN_CHUNK
-    ro = Rollout(n_layers, s.B, s.H, s.d, s.T, s.Nq, s.C, s.topk, window_chunks=2, device=device)
+    ro = Rollout(n_layers, s.B, s.H, s.d, s.T, s.Nq, s.C, s.topk, window_chunks=2, device=device,
+                 overlap=True)
     for l in range(n_layers):
         st = syn.wan_chunk_state(l, device=device)
         ro.layers[l].load(st)
@@ -59,15 +82,8 @@ def time_steps(ro, steps, warmup, torch):
            for _ in range(n_layers)] for _ in range(steps)]
     t0 = time.perf_counter()
     for s in range(steps):
-        t = ro.t
-        for l, L in enumerate(ro.layers):
-            L.select()
-            ev[s][l][0].record()
-            L.fwd()
-            ev[s][l][1].record()
-            if t >= ro.window_chunks:
-                L.update(ro.leaving[t % ro.window_chunks], ro.n_sink)
-            L.append_window(ro.first_slot(t), t * ro.QB)
+        for l in range(n_layers):
+            ro.run_layer(l, fwd_events=ev[s][l])
         ro.advance()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -76,7 +92,9 @@ def time_steps(ro, steps, warmup, torch):
 
 
 def breakdown(ro, torch, reps=3):
-    """Average device time of each call (separate, untimed pass)."""
+    """Average device time of each call, run one after the other on one
+    stream (separate, untimed pass)."""
+    ro.sync_side()
     names = ("select", "fwd", "update", "append")
     acc = {n: [] for n in names}
     for _ in range(reps):
@@ -210,7 +228,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "wan2.1-t2v-1.3b-shaped chunk, steady-state rollout step: "
-                               f"{args.layers} layers x (select + fwd + update + append)",
+                               f"{args.layers} layers x (select + fwd; update + append on a "
+                               "side stream)",
                    "layers": args.layers, "heads": 12, "head_dim": d, "block": 128,
                    "chunk_tokens": 4680, "window_slots": 74, "pool_blocks": 32, "topk": 16,
                    "parallelism": "1 GPU"},
@@ -220,7 +239,8 @@ def main():
         "roofline": {"kernel": "attn_fwd_bf16_kernel<128,128>", "bound": "mfma",
                      "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "launch_us": round(fwd_avg_ms * 1e3, 2),
+                     "traffic": fwd_traffic_bytes(), "traffic_unit": "bytes per launch",
+                     "launch_us": round(fwd_avg_ms * 1e3, 2),
                      "launches": len(fwd_ms)},
         "breakdown_us_per_layer": bd,
     }

@@ -12,7 +12,8 @@
 // chunk's query blocks.
 //
 // All of this is HBM/latency bound and tiny next to the attention: three
-// launches, each far below a microsecond of arithmetic per workgroup.
+// launches (block means; scores + top-k per query block; block mass per
+// head), each written so its global loads are in flight together.
 #include "pbsa_common.h"
 #include "pbsa_internal.h"
 
@@ -34,6 +35,7 @@ __device__ void block_mean_wg(const TIn *__restrict__ src, int n, int d, float *
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
+#pragma unroll 4
   for (int r = rg; r < n; r += rpp) {
     const u32x4 v = *reinterpret_cast<const u32x4 *>(src + (size_t)r * d + cg * E);
     if constexpr (sizeof(TIn) == 2) {
@@ -58,7 +60,7 @@ __device__ void block_mean_wg(const TIn *__restrict__ src, int n, int d, float *
   __syncthreads();
 }
 
-// grid (QB, H, B*2): z even = Q -> qbar (workspace), z odd = K_cur -> kbar_cur
+// grid (QB, H, B*2): z even = Q -> qbar (workspace), z odd = K_cur -> kbar_cur.
 template <typename TIn>
 __global__ __launch_bounds__(256) void chunk_means_kernel(const TIn *__restrict__ q,
                                                           const TIn *__restrict__ k,
@@ -92,102 +94,113 @@ __global__ __launch_bounds__(256) void slot_means_kernel(const TIn *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Coarse scores + window top-k + per-row block softmax.
-// grid (QB, H, B), 256 threads.  Dynamic LDS: s[C+W+QB] floats, flags.
-// Top-k is rank based: a valid window slot is selected iff fewer than k
-// valid slots rank before it in the total order (score desc, id asc, NaN
-// last); its output position is the number of selected slots below it.
-// This is exact and order-independent, so it is deterministic.
+// Coarse scores + window top-k.  grid (QB, H, B), 256 threads.
+//  - candidates [pool C | window W | current QB], 16 lanes per candidate
+//    (coalesced 16-byte reads of kbar, 4 shuffles); all of a pass's loads
+//    are issued before any is used;
+//  - the score row goes to the workspace for the block-mass kernel;
+//  - top-k is rank based: a valid window slot is selected iff fewer than k
+//    valid slots rank before it in the total order (score desc, id asc, NaN
+//    last); its output position is the number of selected slots below it.
+//    Exact and order-independent, hence deterministic.
+// Dynamic LDS: q[128] floats, window ids [W] int64, s[C+W] floats, flags[W].
 // ---------------------------------------------------------------------------
+constexpr int kScorePasses = 8;  // 16 candidates per pass
+
 __global__ __launch_bounds__(256) void score_topk_kernel(
     const float *__restrict__ qbar, const float *__restrict__ kbar_pool,
     const float *__restrict__ kbar_win, const float *__restrict__ kbar_cur,
     const int32_t *__restrict__ pool_count, const int32_t *__restrict__ win_len,
     const int64_t *__restrict__ win_id, int32_t *__restrict__ sel, int32_t *__restrict__ sel_count,
-    float *__restrict__ pi, int H, int d, int T, int W, int C, int QB, int topk, float scale,
+    float *__restrict__ srow_out, int H, int d, int T, int W, int C, int QB, int topk, float scale,
     int32_t *status) {
-  extern __shared__ float smem[];
-  float *qv = smem;                     // [d]
-  float *s = qv + 128;                  // [C + W + QB]
-  int *flag = reinterpret_cast<int *>(s + C + W + QB);  // [W]: 1 valid, 2 selected
-  __shared__ float red[8];
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  float *qv = smem;                                        // [128]
+  int64_t *wid = reinterpret_cast<int64_t *>(qv + 128);   // [W]
+  float *s = reinterpret_cast<float *>(wid + W);          // [C + W]
+  int *flag = reinterpret_cast<int *>(s + C + W);         // [W]: 1 valid, 2 selected
   __shared__ int nvalid_sh;
 
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t bh = (size_t)b * H + h;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   int n_pool = pool_count[bh];
   if (n_pool < 0 || n_pool > C) {
     if (t == 0) set_status(status, PBSA_STATUS_POOL_COUNT);
     n_pool = max(0, min(n_pool, C));
   }
   if (t < d) qv[t] = qbar[(bh * QB + i) * d + t];
+  int nv = 0;
+  for (int w = t; w < W; w += 256) {
+    const int len = win_len[w];
+    if (len > T) set_status(status, PBSA_STATUS_WIN_LEN);
+    flag[w] = len > 0 ? 1 : 0;
+    nv += len > 0;
+    wid[w] = win_id[w];
+  }
   if (t == 0) nvalid_sh = 0;
   __syncthreads();
+  for (int o = 32; o > 0; o >>= 1) nv += __shfl_xor(nv, o);
+  if (lane == 0) atomicAdd(&nvalid_sh, nv);
 
-  const int nj = C + W + QB;  // candidate layout: [pool C | window W | current QB]
-  for (int j = t; j < nj; j += 256) {
-    const float *kb = nullptr;
-    bool valid;
-    if (j < C) {
-      valid = j < n_pool;
-      kb = kbar_pool + (bh * C + j) * d;
-    } else if (j < C + W) {
-      const int w = j - C;
-      const int len = win_len[w];
-      valid = len > 0;
-      if (len > T && t == 0) set_status(status, PBSA_STATUS_WIN_LEN);
-      kb = kbar_win + (bh * W + w) * d;
-      flag[w] = valid ? 1 : 0;
-    } else {
-      valid = true;
-      kb = kbar_cur + (bh * QB + (j - C - W)) * d;
-    }
-    float acc = 0.f;
-    if (valid) {
-      for (int e = 0; e < d; e += 4) {
-        const f32x4 kv4 = *reinterpret_cast<const f32x4 *>(kb + e);
-        acc += qv[e] * kv4[0];
-        acc += qv[e + 1] * kv4[1];
-        acc += qv[e + 2] * kv4[2];
-        acc += qv[e + 3] * kv4[3];
+  const int nj = C + W + QB;
+  const int sub = lane >> 4, sl = lane & 15;
+  const int per = d / 16;  // floats per lane (8 or 4)
+  float *srow = srow_out + (bh * QB + i) * (size_t)nj;
+  for (int base = wave * 4; base < nj; base += 16 * kScorePasses) {
+    f32x4 k0[kScorePasses], k1[kScorePasses];
+    bool ok[kScorePasses];
+#pragma unroll
+    for (int ps = 0; ps < kScorePasses; ++ps) {
+      const int j = base + ps * 16 + sub;
+      const float *kb = kbar_pool;
+      bool valid = false;
+      if (j < C) {
+        valid = j < n_pool;
+        kb = kbar_pool + (bh * C + j) * d;
+      } else if (j < C + W) {
+        valid = flag[j - C] != 0;
+        kb = kbar_win + (bh * W + (j - C)) * d;
+      } else if (j < nj) {
+        valid = true;
+        kb = kbar_cur + (bh * QB + (j - C - W)) * d;
       }
-      acc *= scale;
+      ok[ps] = valid;
+      k0[ps] = f32x4{0.f, 0.f, 0.f, 0.f};
+      k1[ps] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (valid) {
+        k0[ps] = *reinterpret_cast<const f32x4 *>(kb + sl * per);
+        if (per == 8) k1[ps] = *reinterpret_cast<const f32x4 *>(kb + sl * per + 4);
+      }
     }
-    s[j] = valid ? acc : -INFINITY;
+#pragma unroll
+    for (int ps = 0; ps < kScorePasses; ++ps) {
+      const int j = base + ps * 16 + sub;
+      const float *qq = qv + sl * per;
+      float acc = qq[0] * k0[ps][0] + qq[1] * k0[ps][1] + qq[2] * k0[ps][2] + qq[3] * k0[ps][3];
+      if (per == 8) acc += qq[4] * k1[ps][0] + qq[5] * k1[ps][1] + qq[6] * k1[ps][2] + qq[7] * k1[ps][3];
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      acc += __shfl_xor(acc, 4);
+      acc += __shfl_xor(acc, 8);
+      if (sl == 0 && j < nj) {
+        const float v = ok[ps] ? acc * scale : -INFINITY;
+        srow[j] = v;
+        if (j < C + W) s[j] = v;
+      }
+    }
   }
   __syncthreads();
 
-  // row max / sum over the valid candidates (NaN propagates through the sum)
-  float mx = -INFINITY;
-  for (int j = t; j < nj; j += 256) mx = fmaxf(mx, s[j]);
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  if ((t & 63) == 0) red[t >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float sum = 0.f;
-  for (int j = t; j < nj; j += 256) sum += expf(s[j] - mx);  // invalid: exp(-inf) = 0
-  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-  if ((t & 63) == 0) red[4 + (t >> 6)] = sum;
-  __syncthreads();
-  sum = (red[4] + red[5]) + (red[6] + red[7]);
-  const float inv = 1.f / sum;
-  float *pirow = pi + (bh * QB + i) * (size_t)(C + W);
-  for (int j = t; j < C + W; j += 256) pirow[j] = expf(s[j] - mx) * inv;
-
   // rank-based top-k over the valid window slots
-  int cnt = 0;
-  for (int w = t; w < W; w += 256) cnt += flag[w] & 1;
-  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
-  if ((t & 63) == 0) atomicAdd(&nvalid_sh, cnt);
   for (int w = t; w < W; w += 256) {
     if (!(flag[w] & 1)) continue;
     const float sw = s[C + w];
-    const int64_t iw = win_id[w];
+    const int64_t iw = wid[w];
     int rank = 0;
+#pragma unroll 8
     for (int v = 0; v < W; ++v)
-      if ((flag[v] & 1) && v != w && ranks_before(s[C + v], win_id[v], sw, iw)) ++rank;
+      rank += (flag[v] & 1) && v != w && ranks_before(s[C + v], wid[v], sw, iw);
     if (rank < topk) flag[w] |= 2;
   }
   __syncthreads();
@@ -196,6 +209,7 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
   for (int w = t; w < W; w += 256) {
     if (!(flag[w] & 2)) continue;
     int pos = 0;
+#pragma unroll 8
     for (int v = 0; v < w; ++v) pos += (flag[v] >> 1) & 1;
     selrow[pos] = w;
   }
@@ -203,21 +217,69 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
   if (t == 0) sel_count[bh * QB + i] = n_sel;
 }
 
-// mass[j] = sum_i pi[i][j] in ascending i (deterministic).  grid (H, B).
-__global__ __launch_bounds__(256) void mass_reduce_kernel(const float *__restrict__ pi,
-                                                          float *__restrict__ mass_pool,
-                                                          float *__restrict__ mass_win, int H,
-                                                          int W, int C, int QB) {
+// ---------------------------------------------------------------------------
+// Block mass per (b, h): M_j = sum_i softmax_j(s_i.), the softmax over every
+// candidate of query block i (pool, window and current blocks); written for
+// the pool and window slots (0 where invalid).  One workgroup of 1024
+// threads per (b, h) (latency bound: many waves in flight); the score rows
+// are staged into LDS in chunks of rows; sums run over i in ascending order
+// (deterministic).  grid (H, B).
+// ---------------------------------------------------------------------------
+constexpr int kMassLds = 12288;  // floats of staged scores
+constexpr int kMassThreads = 1024;
+
+__global__ __launch_bounds__(kMassThreads) void block_mass_kernel(const float *__restrict__ srows,
+                                                                  float *__restrict__ mass_pool,
+                                                                  float *__restrict__ mass_win,
+                                                                  int H, int W, int C, int QB) {
+  __shared__ float sbuf[kMassLds];
+  __shared__ float rmax[kMassThreads / 64 * 16], rinv[kMassThreads / 64 * 16];
   const size_t bh = (size_t)blockIdx.y * H + blockIdx.x;
-  const int CW = C + W;
-  for (int j = threadIdx.x; j < CW; j += 256) {
-    const float *col = pi + bh * QB * (size_t)CW + j;
-    float s = 0.f;
-    for (int i = 0; i < QB; ++i) s += col[(size_t)i * CW];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  constexpr int NWV = kMassThreads / 64;
+  const int nj = C + W + QB;
+  const int rows_per = max(1, min(NWV * 16, kMassLds / nj));
+  const float *src = srows + bh * QB * (size_t)nj;
+  float acc[2] = {0.f, 0.f};  // columns t and t + 1024 (C + W <= 2048)
+  for (int r0 = 0; r0 < QB; r0 += rows_per) {
+    const int nr = min(rows_per, QB - r0);
+    __syncthreads();
+    const float *s0 = src + (size_t)r0 * nj;
+#pragma unroll 8
+    for (int e = t; e < nr * nj; e += kMassThreads) sbuf[e] = s0[e];
+    __syncthreads();
+    // per-row max and 1/sum, one wave per row
+    for (int r = wave; r < nr; r += NWV) {
+      float mx = -INFINITY;
+      for (int j = lane; j < nj; j += 64) mx = fmaxf(mx, sbuf[r * nj + j]);
+      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      float sm = 0.f;
+      for (int j = lane; j < nj; j += 64) sm += __expf(sbuf[r * nj + j] - mx);
+      for (int o = 32; o > 0; o >>= 1) sm += __shfl_xor(sm, o);
+      if (lane == 0) {
+        rmax[r] = mx;
+        rinv[r] = 1.f / sm;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int j = t + kMassThreads * q;
+      if (j < C + W) {
+        float a = acc[q];
+#pragma unroll 4
+        for (int r = 0; r < nr; ++r) a += __expf(sbuf[r * nj + j] - rmax[r]) * rinv[r];
+        acc[q] = a;
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int j = t + kMassThreads * q;
     if (j < C)
-      mass_pool[bh * C + j] = s;
-    else
-      mass_win[bh * W + (j - C)] = s;
+      mass_pool[bh * C + j] = acc[q];
+    else if (j < C + W)
+      mass_win[bh * W + (j - C)] = acc[q];
   }
 }
 
@@ -259,12 +321,12 @@ __global__ __launch_bounds__(256) void window_append_kernel(
 size_t select_ws_bytes(const pbsa_problem &p) {
   const size_t QB = (p.Nq + p.T - 1) / p.T;
   const size_t bh = (size_t)p.B * p.H;
-  return align256(bh * QB * p.d * sizeof(float)) + align256(bh * QB * (p.C + p.W) * sizeof(float));
+  return align256(bh * QB * p.d * sizeof(float)) +
+         align256(bh * QB * (p.C + p.W + QB) * sizeof(float));
 }
 
 size_t select_lds_bytes(const pbsa_problem &p) {
-  const int QB = (p.Nq + p.T - 1) / p.T;
-  return (128 + (size_t)p.C + p.W + QB) * sizeof(float) + (size_t)p.W * sizeof(int);
+  return (128 + (size_t)p.C + p.W) * sizeof(float) + (size_t)p.W * (sizeof(int) + sizeof(int64_t));
 }
 
 hipError_t launch_select(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
@@ -273,8 +335,8 @@ hipError_t launch_select(const pbsa_problem &p, float scale, const void *q, cons
   const int QB = (p.Nq + p.T - 1) / p.T;
   const size_t bh = (size_t)p.B * p.H;
   float *qbar = reinterpret_cast<float *>(ws);
-  float *pi = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) +
-                                        align256(bh * QB * p.d * sizeof(float)));
+  char *wsb = reinterpret_cast<char *>(ws);
+  float *srows = reinterpret_cast<float *>(wsb + align256(bh * QB * p.d * sizeof(float)));
   dim3 g1(QB, p.H, p.B * 2);
   if (p.dtype == PBSA_BF16)
     chunk_means_kernel<uint16_t><<<g1, 256, 0, st>>>(
@@ -285,9 +347,10 @@ hipError_t launch_select(const pbsa_problem &p, float scale, const void *q, cons
   dim3 g2(QB, p.H, p.B);
   score_topk_kernel<<<g2, 256, select_lds_bytes(p), st>>>(
       qbar, kv.kbar_pool, kv.kbar_win, kv.kbar_cur, kv.pool_count, kv.win_len, kv.win_id, sel,
-      sel_count, pi, p.H, p.d, p.T, p.W, p.C, QB, p.topk, scale, p.dev_status);
-  dim3 g3(p.H, p.B);
-  mass_reduce_kernel<<<g3, 256, 0, st>>>(pi, mass_pool, mass_win, p.H, p.W, p.C, QB);
+      sel_count, srows, p.H, p.d, p.T, p.W, p.C, QB, p.topk, scale, p.dev_status);
+  if (p.C + p.W > 0)
+    block_mass_kernel<<<dim3(p.H, p.B), kMassThreads, 0, st>>>(srows, mass_pool, mass_win, p.H, p.W,
+                                                                p.C, QB);
   return hipGetLastError();
 }
 

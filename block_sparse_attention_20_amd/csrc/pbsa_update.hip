@@ -34,6 +34,8 @@ __global__ __launch_bounds__(256) void update_decide_kernel(
   __shared__ int8_t xkeep[kMaxX];
   __shared__ int8_t cflag[kMaxLeave];
   __shared__ int32_t free_slot[kMaxC];
+  __shared__ int32_t lw[kMaxLeave], lwl[kMaxLeave];
+  __shared__ int64_t lid[kMaxLeave];
   __shared__ int red[4];
 
   const int t = threadIdx.x;
@@ -48,31 +50,34 @@ __global__ __launch_bounds__(256) void update_decide_kernel(
     xm[p] = mass_pool[bh * C + p];
     xsrc[p] = p;
   }
+  // stage the leaving slots' metadata (wl = -1 marks a slot out of range)
+  for (int c = t; c < n_leave; c += 256) {
+    const int w = leaving[c];
+    const bool inr = w >= 0 && w < W;
+    if (!inr) set_status(status, PBSA_STATUS_SEL);
+    lw[c] = w;
+    lwl[c] = inr ? win_len[w] : -1;
+    lid[c] = inr ? win_id[w] : -1;
+  }
   __syncthreads();
   // candidate filter: slot in range, non-empty, not pooled, first of its id
   for (int c = t; c < n_leave; c += 256) {
-    const int w = leaving[c];
-    bool ok = w >= 0 && w < W;
-    if (!ok) set_status(status, PBSA_STATUS_SEL);
-    int64_t id = 0;
-    if (ok) {
-      ok = win_len[w] > 0;
-      id = win_id[w];
-    }
-    for (int p = 0; ok && p < n_pool; ++p) ok = xid[p] != id;
-    for (int c2 = 0; ok && c2 < c; ++c2) {
-      const int w2 = leaving[c2];
-      if (w2 >= 0 && w2 < W && win_len[w2] > 0 && win_id[w2] == id) ok = false;
-    }
+    const int64_t id = lid[c];
+    bool ok = lwl[c] > 0;
+#pragma unroll 8
+    for (int p = 0; p < n_pool; ++p) ok = ok && xid[p] != id;
+#pragma unroll 8
+    for (int c2 = 0; c2 < c; ++c2) ok = ok && !(lwl[c2] > 0 && lid[c2] == id);
     cflag[c] = ok ? 1 : 0;
   }
   __syncthreads();
   for (int c = t; c < n_leave; c += 256) {
     if (!cflag[c]) continue;
     int pos = n_pool;
+#pragma unroll 8
     for (int c2 = 0; c2 < c; ++c2) pos += cflag[c2];
-    const int w = leaving[c];
-    xid[pos] = win_id[w];
+    const int w = lw[c];
+    xid[pos] = lid[c];
     xm[pos] = mass_win[bh * W + w];
     xsrc[pos] = -1 - w;
   }
@@ -102,8 +107,10 @@ __global__ __launch_bounds__(256) void update_decide_kernel(
       keep = true;
     } else {
       int r = 0;
-      for (int y = 0; y < n_x; ++y)
-        r += (xid[y] >= n_sink) && ranks_before(xm[y], xid[y], xm[x], xid[x]);
+      const float mxx = xm[x];
+      const int64_t ixx = xid[x];
+#pragma unroll 8
+      for (int y = 0; y < n_x; ++y) r += (xid[y] >= n_sink) && ranks_before(xm[y], xid[y], mxx, ixx);
       keep = r < C - n_pin;
     }
     xkeep[x] = keep ? 1 : 0;
@@ -114,6 +121,7 @@ __global__ __launch_bounds__(256) void update_decide_kernel(
     const bool fr = s >= n_pool || !xkeep[s];
     if (!fr) continue;
     int pos = 0;
+#pragma unroll 8
     for (int s2 = 0; s2 < s; ++s2) pos += (s2 >= n_pool || !xkeep[s2]);
     free_slot[pos] = s;
   }
@@ -123,13 +131,15 @@ __global__ __launch_bounds__(256) void update_decide_kernel(
     nk += xkeep[x];
     if (x < n_pool || !xkeep[x]) continue;
     int pos = 0;  // rank among the admitted by id (ids are unique)
-    for (int y = n_pool; y < n_x; ++y) pos += xkeep[y] && xid[y] < xid[x];
+    const int64_t ixx = xid[x];
+#pragma unroll 8
+    for (int y = n_pool; y < n_x; ++y) pos += xkeep[y] && xid[y] < ixx;
     const int slot = free_slot[pos];
     const int w = -1 - xsrc[x];
     a_slot[bh * C + pos] = slot;
     a_src[bh * C + pos] = w;
     pool_len[bh * C + slot] = min(max(win_len[w], 0), T);
-    pool_id[bh * C + slot] = win_id[w];
+    pool_id[bh * C + slot] = xid[x];
     ++na;
   }
   for (int o = 32; o > 0; o >>= 1) {

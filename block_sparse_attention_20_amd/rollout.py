@@ -17,6 +17,13 @@ Per layer and chunk t (all device work is libpbsa.so; nothing syncs):
      t mod window_chunks), block ids t*QB + j.
 The state of a layer is plain device tensors (``PBSALayer.t``), so it can be
 saved and restored with ``state_dict`` / ``load_state_dict``.
+
+With ``overlap=True`` steps 2-3 go to a side stream: the next layer needs
+only this layer's output O, while the updated pool and window are needed by
+the next *chunk*.  The side stream waits for the layer's forward (the update
+rewrites pool slots the forward reads); the next chunk's select of the layer
+and the next write of its inputs wait for the side work.  Both streams keep
+the default priority.
 """
 from __future__ import annotations
 
@@ -33,7 +40,7 @@ STATE_KEYS = ("k_win", "v_win", "win_len", "win_id", "kbar_win", "k_pool", "v_po
 class Rollout:
     def __init__(self, n_layers: int, B: int, H: int, d: int, T: int, Nq: int, C: int, topk: int,
                  n_sink: int = 0, window_chunks: int = 2, dtype=torch.bfloat16, scale: float = 0.0,
-                 device="cuda"):
+                 device="cuda", overlap: bool = False):
         self.QB = (Nq + T - 1) // T
         self.window_chunks = window_chunks
         self.W = window_chunks * self.QB
@@ -44,26 +51,59 @@ class Rollout:
         self.leaving = [torch.arange(p * self.QB, (p + 1) * self.QB, dtype=torch.int32, device=device)
                         for p in range(window_chunks)]
         self.t = 0
+        self.side = torch.cuda.Stream(device=device) if overlap else None
+        self.ev_fwd = [torch.cuda.Event() for _ in range(n_layers)] if overlap else None
+        self.ev_side = [torch.cuda.Event() for _ in range(n_layers)] if overlap else None
+        self.side_pending = [False] * n_layers
+
+    def _wait_side(self, layer: int):
+        if self.side is not None and self.side_pending[layer]:
+            torch.cuda.current_stream().wait_event(self.ev_side[layer])
+            self.side_pending[layer] = False
 
     def first_slot(self, chunk: int) -> int:
         return (chunk % self.window_chunks) * self.QB
 
     def set_inputs(self, layer: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+        self._wait_side(layer)   # the window append still reads k_cur / v_cur
         L = self.layers[layer]
         L.t["q"].copy_(q)
         L.t["k_cur"].copy_(k)
         L.t["v_cur"].copy_(v)
 
-    def run_layer(self, layer: int, attention: bool = True):
-        """PBSA work of one layer for the current chunk (inputs already set)."""
+    def run_layer(self, layer: int, attention: bool = True, fwd_events=None):
+        """PBSA work of one layer for the current chunk (inputs already set).
+        ``fwd_events``: optional (start, end) events recorded around the
+        forward launch on the current stream."""
         L = self.layers[layer]
         t = self.t
+        self._wait_side(layer)
         L.select()
         if attention:
+            if fwd_events is not None:
+                fwd_events[0].record()
             L.fwd()
+            if fwd_events is not None:
+                fwd_events[1].record()
+        if self.side is None:
+            self._side_work(L, t)
+            return
+        self.ev_fwd[layer].record()
+        with torch.cuda.stream(self.side):
+            self.side.wait_event(self.ev_fwd[layer])
+            self._side_work(L, t)
+            self.ev_side[layer].record(self.side)
+        self.side_pending[layer] = True
+
+    def _side_work(self, L, t):
         if t >= self.window_chunks:
             L.update(self.leaving[t % self.window_chunks], self.n_sink)
         L.append_window(self.first_slot(t), t * self.QB)
+
+    def sync_side(self):
+        """Make the current stream wait for every layer's side work."""
+        for l in range(len(self.layers)):
+            self._wait_side(l)
 
     def run_chunk(self, attention: bool = True):
         for l in range(len(self.layers)):
@@ -75,10 +115,12 @@ class Rollout:
 
     # -- checkpoint / resume ---------------------------------------------------
     def state_dict(self) -> dict:
+        self.sync_side()
         return {"t": self.t,
                 "layers": [{k: L.t[k].clone() for k in STATE_KEYS} for L in self.layers]}
 
     def load_state_dict(self, sd: dict):
+        self.sync_side()
         self.t = int(sd["t"])
         for L, s in zip(self.layers, sd["layers"]):
             for k in STATE_KEYS:

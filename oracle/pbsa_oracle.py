@@ -250,7 +250,7 @@ def as_f64_state(st: dict) -> dict:
             v = v.detach().to("cpu")
             v = v.double().numpy() if v.is_floating_point() else v.long().numpy()
         elif isinstance(v, np.ndarray):
-            v = v.astype(F64) if v.dtype.kind == "f" else v.astype(np.int64)
+            v = v.astype(F64, copy=False) if v.dtype.kind == "f" else v.astype(np.int64, copy=False)
         out[key] = v
     return out
 

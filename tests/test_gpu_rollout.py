@@ -100,6 +100,30 @@ def test_rollout_checkpoint_resume_bitwise():
         assert torch.equal(x, y)
 
 
+def test_rollout_side_stream_overlap_is_bitwise_identical():
+    """Update + append on a side stream (overlapped with the next layers)
+    gives exactly the serial result, over several layers and chunks."""
+    shape = syn.Shape(B=1, H=2, d=128, T=128, Nq=300, W=0, C=4, topk=3)
+    chunks = make_chunks(shape, 6)
+    outs = {}
+    for overlap in (False, True):
+        ro = Rollout(3, 1, 2, 128, 128, 300, 4, 3, overlap=overlap)
+        res = []
+        for ch in chunks:
+            for l in range(3):
+                ro.set_inputs(l, ch["q"].cuda(), ch["k"].cuda(), ch["v"].cuda())
+                ro.run_layer(l)
+                res.append(ro.layers[l].t["o"].clone())
+            ro.advance()
+        ro.sync_side()
+        torch.cuda.synchronize()
+        res.append(ro.layers[2].t["k_pool"].clone())
+        res.append(ro.layers[1].t["pool_id"].clone())
+        outs[overlap] = res
+    for a, b in zip(outs[False], outs[True]):
+        assert torch.equal(a, b)
+
+
 def test_rollout_work_is_flat_once_pool_full():
     """Pool empty for chunks 0-2, QB blocks after chunk 3's update... full (C)
     from chunk 4 on; every query block selects k window blocks once the
