@@ -113,40 +113,141 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // s_waitcnt immediate: vmcnt <= n, expcnt and lgkmcnt unconstrained (gfx9 encoding)
 #define PBSA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14)))
 
-// Stage one [BT][D] bf16 block (rows >= len read as zeros) into LDS with the
-// 16-byte chunks of each row XOR-permuted by a row-dependent swizzle (K:
-// row & 7; V: 2 (row & 7), or 2 (row & 3) when a row has 8 chunks).  Each
-// wave moves IPW chunks of 1 KB with global_load_lds_dwordx4 (lane l lands
-// at base + 16 l), so the whole block is in flight without touching VGPRs.
-// Every wave's first row is a multiple of 8, so the swizzle depends only on
-// the lane and the instruction index.
+// LDS swizzles (gfx950 LDS: 64 banks of 4 bytes; a 16-byte read serves 16
+// lanes per cycle, an 8-byte read 32 lanes).  Rows are 16-byte chunks; the
+// physical chunk of logical chunk c in row r is c ^ swz(r).
+//  K (read as MFMA A rows: 16 consecutive rows, one chunk each):
+//    d = 128: r & 15 (16 distinct chunks); d = 64: (r >> 1) & 7 with two rows
+//    per 256-byte bank line.
+//  V (read with ds_read_b64_tr_b16: 4 consecutive rows x 64 bytes per 32
+//    lanes): d = 128: 4 (r & 3) moves each row's 64-byte group to its own
+//    quarter of the bank line; d = 64: 2 (r & 3).
+template <int D, bool V>
+__device__ __forceinline__ int lds_swz(int r) {
+  if constexpr (V) return D == 128 ? 4 * (r & 3) : 2 * (r & 3);
+  else return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// Stage one [BT][D] bf16 block (rows >= len read as zeros) into LDS,
+// swizzled as above.  Each wave moves IPW chunks of 1 KB with
+// global_load_lds_dwordx4 (lane l lands at base + 16 l), so the whole block
+// is in flight without touching VGPRs.  Instruction `it` of a wave covers
+// rows row0 + it*RPI + lane/CPR; every wave's first row is a multiple of 16,
+// so a lane's source offset within its row band repeats every 16/RPI
+// instructions: dma_lane_offsets() computes those few byte offsets once.
+template <int D, int BT, int NW>
+struct DmaGeom {
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;          // rows per 1 KB instruction
+  static constexpr int IPW = BT * D * 2 / 1024 / NW;
+  static constexpr int NVAR = 16 / RPI < IPW ? 16 / RPI : IPW;  // distinct lane offsets
+  static_assert((IPW * RPI) % 16 == 0, "wave row ranges must start at multiples of 16");
+};
+
+template <int D, int BT, int NW, bool VSWZ>
+__device__ __forceinline__ void dma_lane_offsets(int lane, uint32_t (&ofs)[DmaGeom<D, BT, NW>::NVAR]) {
+  using G = DmaGeom<D, BT, NW>;
+  const int p = lane % G::CPR, rsub = lane / G::CPR;
+#pragma unroll
+  for (int v = 0; v < G::NVAR; ++v) {
+    const int rl = v * G::RPI + rsub;
+    ofs[v] = (uint32_t)((rl * D + (p ^ lds_swz<D, VSWZ>(rl)) * 8) * 2);
+  }
+}
+
+// Ragged block (len < BT): rows past len come from the zero page.
+template <int D, int BT, int NW>
+__device__ __forceinline__ void dma_block_ragged(uint16_t *dst, const char *base, int row0,
+                                                          int len, int lane,
+                                                          const uint32_t *ofs) {
+  using G = DmaGeom<D, BT, NW>;
+  const int rsub = lane / G::CPR, p = lane % G::CPR;
+#pragma unroll
+  for (int it = 0; it < G::IPW; ++it) {
+    const bool ok = row0 + it * G::RPI + rsub < len;
+    const char *g = ok ? base + (it / G::NVAR) * (G::NVAR * G::RPI * D * 2) + ofs[it % G::NVAR]
+                       : reinterpret_cast<const char *>(g_zero_rows + p * 4);
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)(dst + it * 512), 16, 0, 0);
+  }
+}
+
 template <int D, int BT, int NW, bool VSWZ>
 __device__ __forceinline__ void dma_block(uint16_t *lds, const uint16_t *src, int len, int wave,
-                                          int lane) {
-  constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;         // rows per 1 KB instruction
-  constexpr int IPW = BT * D * 2 / 1024 / NW;
-  static_assert((IPW * RPI) % 8 == 0, "wave row ranges must start at multiples of 8");
-  const int p = lane % CPR, rsub = lane / CPR;
-  const int row0 = wave * IPW * RPI;
-  uint16_t *dst = lds + wave * IPW * 512;
+                                          int lane, const uint32_t (&ofs)[DmaGeom<D, BT, NW>::NVAR]) {
+  using G = DmaGeom<D, BT, NW>;
+  const int row0 = wave * G::IPW * G::RPI;
+  const char *base = reinterpret_cast<const char *>(src + (size_t)row0 * D);
+  uint16_t *dst = lds + wave * G::IPW * 512;
   if (len >= BT) {
 #pragma unroll
-    for (int it = 0; it < IPW; ++it) {
-      const int rl = it * RPI + rsub;  // row - row0
-      const int sw = VSWZ ? (CPR == 16 ? 2 * (rl & 7) : 2 * (rl & 3)) : (rl & 7);
-      __builtin_amdgcn_global_load_lds(src + (size_t)(row0 + rl) * D + (p ^ sw) * 8,
-                                       (lds_void *)(dst + it * 512), 16, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int it = 0; it < IPW; ++it) {
-      const int rl = it * RPI + rsub;
-      const int sw = VSWZ ? (CPR == 16 ? 2 * (rl & 7) : 2 * (rl & 3)) : (rl & 7);
-      const void *g = row0 + rl < len ? (const void *)(src + (size_t)(row0 + rl) * D + (p ^ sw) * 8)
-                                      : (const void *)(g_zero_rows + p * 4);
+    for (int it = 0; it < G::IPW; ++it) {
+      const char *g = base + (it / G::NVAR) * (G::NVAR * G::RPI * D * 2) + ofs[it % G::NVAR];
       __builtin_amdgcn_global_load_lds(g, (lds_void *)(dst + it * 512), 16, 0, 0);
     }
+  } else {
+    dma_block_ragged<D, BT, NW>(dst, base, row0, len, lane, ofs);
+  }
+}
+
+// The pool and selected-window part of a query block's list, resolved once
+// per workgroup into LDS: element offset of the block in its region and
+// (len | window << 16).  Entries past kMaxList fall back to resolve_block.
+constexpr int kMaxList = 128;
+
+struct BlockList {
+  int64_t off[kMaxList];
+  int32_t meta[kMaxList];
+};
+
+template <int D, int BT>
+__device__ __forceinline__ void preload_list(const FwdArgs &a, size_t bh, int i, int n_pool, int sc,
+                                             BlockList &bl, int t) {
+  const int n = min(n_pool + sc, kMaxList);
+  for (int j = t; j < n; j += 2 * BT) {
+    int64_t off;
+    int len, win = 0;
+    if (j < n_pool) {
+      off = (int64_t)(bh * a.C + j) * (BT * D);
+      len = a.pool_len[bh * a.C + j];
+    } else {
+      const int w = a.sel[(bh * a.QB + i) * (size_t)a.topk + (j - n_pool)];
+      win = 1;
+      if (w < 0 || w >= a.W) {
+        set_status(a.status, PBSA_STATUS_SEL);
+        off = 0;
+        len = 0;
+      } else {
+        off = (int64_t)(bh * a.W + w) * (BT * D);
+        len = a.win_len[w];
+      }
+    }
+    if (len < 0 || len > BT) {
+      set_status(a.status, PBSA_STATUS_WIN_LEN);
+      len = max(0, min(len, BT));
+    }
+    bl.off[j] = off;
+    bl.meta[j] = len | (win << 16);
+  }
+}
+
+template <int D, int BT>
+__device__ __forceinline__ void list_block(const FwdArgs &a, const BlockList &bl, size_t bh, int i,
+                                           int n_pool, int sc, int j, const uint16_t *&kp,
+                                           const uint16_t *&vp, int &len) {
+  if (j < n_pool + sc && j < kMaxList) {
+    const int64_t off = __builtin_amdgcn_readfirstlane((int)(bl.off[j] & 0xffffffff)) |
+                        ((int64_t)__builtin_amdgcn_readfirstlane((int)(bl.off[j] >> 32)) << 32);
+    const int meta = __builtin_amdgcn_readfirstlane(bl.meta[j]);
+    len = meta & 0xffff;
+    if (meta >> 16) {
+      kp = (const uint16_t *)a.k_win + off;
+      vp = (const uint16_t *)a.v_win + off;
+    } else {
+      kp = (const uint16_t *)a.k_pool + off;
+      vp = (const uint16_t *)a.v_pool + off;
+    }
+  } else {
+    resolve_block<uint16_t, D, BT>(a, bh, i, n_pool, sc, j, kp, vp, len);
   }
 }
 
@@ -157,6 +258,7 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   constexpr int IPW = BT * D * 2 / 1024 / NW;
   __shared__ __attribute__((aligned(1024))) uint16_t Kl[BT * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vl[BT * D];
+  __shared__ BlockList blist;
 
   int item;
   item_of_block(a, item);
@@ -187,7 +289,7 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f;  // running max (log2 units) and row sum
   const float sl2 = a.sl2;
 
   // Per-lane LDS element offsets, fixed for the whole kernel (the swizzle of
@@ -195,24 +297,29 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   // K fragment (A of S^T): row tt*32 + l32, logical chunk 2kk + g.
   int koff[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = l32 * D + (((2 * kk + g) ^ (l32 & 7)) * 8);
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = l32 * D + (((2 * kk + g) ^ lds_swz<D, false>(l32)) * 8);
   // V^T fragment via ds_read_b64_tr_b16: in each 16-lane group, lane gi
   // addresses row gi/4 of a 4-row band (rows tt*32 + 16h + 4g + gi/4, and the
   // band 8 rows further) and 4 of the group's 16 dims; it receives dim gi of
   // the 4 rows.
   const int gi = lane & 15, q16 = (lane >> 4) & 1;
   const int vr = gi >> 2, vq = gi & 3;
-  const int vsw = CPR == 16 ? 2 * ((4 * g + vr) & 7) : 2 * ((4 * g + vr) & 3);
+  const int vsw = lds_swz<D, true>(4 * g + vr);  // rows step*16 + 4g + vr (+8) share it
   int voff[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
     voff[dt] = (4 * g + vr) * D + (((4 * dt + 2 * q16 + (vq >> 1)) ^ vsw) * 8) + (vq & 1) * 4;
 
+  uint32_t kdma[DmaGeom<D, BT, NW>::NVAR], vdma[DmaGeom<D, BT, NW>::NVAR];
+  dma_lane_offsets<D, BT, NW, false>(lane, kdma);
+  dma_lane_offsets<D, BT, NW, true>(lane, vdma);
+  preload_list<D, BT>(a, bh, i, n_pool, sc, blist, t);
+  __syncthreads();
   const uint16_t *kp, *vp;
   int len;
-  resolve_block<uint16_t, D, BT>(a, bh, i, n_pool, sc, 0, kp, vp, len);
-  dma_block<D, BT, NW, false>(Kl, kp, len, wave, lane);
-  dma_block<D, BT, NW, true>(Vl, vp, len, wave, lane);
+  list_block<D, BT>(a, blist, bh, i, n_pool, sc, 0, kp, vp, len);
+  dma_block<D, BT, NW, false>(Kl, kp, len, wave, lane, kdma);
+  dma_block<D, BT, NW, true>(Vl, vp, len, wave, lane, vdma);
   PBSA_WAIT_VM(0);
   __syncthreads();
 
@@ -224,19 +331,28 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     for (int tt = 0; tt < BT / 32; ++tt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[tt][e] = 0.f;
+    {
+      bf16x8 ka[2][BT / 32];  // K fragments, one k-step ahead of the MFMAs
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
+      for (int tt = 0; tt < BT / 32; ++tt)
+        ka[0][tt] = *reinterpret_cast<const bf16x8 *>(&Kl[tt * 32 * D + koff[0]]);
 #pragma unroll
-      for (int tt = 0; tt < BT / 32; ++tt) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&Kl[tt * 32 * D + koff[kk]]);
-        sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc[tt], 0, 0, 0);
+      for (int kk = 0; kk < D / 16; ++kk) {
+        if (kk + 1 < D / 16) {
+#pragma unroll
+          for (int tt = 0; tt < BT / 32; ++tt)
+            ka[(kk + 1) & 1][tt] = *reinterpret_cast<const bf16x8 *>(&Kl[tt * 32 * D + koff[kk + 1]]);
+        }
+#pragma unroll
+        for (int tt = 0; tt < BT / 32; ++tt)
+          sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk & 1][tt], qf[kk], sacc[tt], 0, 0, 0);
       }
     }
     __syncthreads();  // every wave is done with K
     const bool more = j + 1 < nb;
     if (more) {
-      resolve_block<uint16_t, D, BT>(a, bh, i, n_pool, sc, j + 1, kp, vp, len);
-      dma_block<D, BT, NW, false>(Kl, kp, len, wave, lane);
+      list_block<D, BT>(a, blist, bh, i, n_pool, sc, j + 1, kp, vp, len);
+      dma_block<D, BT, NW, false>(Kl, kp, len, wave, lane, kdma);
     }
     // ---- online softmax (log2 domain); the running max only moves when a
     // block raises it by more than 8, so O is rarely rescaled and P <= 2^8.
@@ -269,11 +385,25 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     if (!more) PBSA_WAIT_VM(0);
     else PBSA_WAIT_VM(IPW);  // V of this block has landed (K of the next may be in flight)
     __syncthreads();
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T  (V^T fragments read one step ahead)
+    {
+      auto vfrag = [&](int step, int dt) -> bf16x8 {
+        const int r1 = step * 16 * D + voff[dt];  // step = 2*tt + h
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&Vl[r1]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&Vl[r1 + 8 * D]));
+        return __builtin_bit_cast(bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){
+                                              lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      };
+      bf16x8 va[2][D / 32];
 #pragma unroll
-    for (int tt = 0; tt < BT / 32; ++tt) {
+      for (int dt = 0; dt < D / 32; ++dt) va[0][dt] = vfrag(0, dt);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int st = 0; st < BT / 16; ++st) {
+        const int tt = st >> 1, h = st & 1;
+        if (st + 1 < BT / 16) {
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) va[(st + 1) & 1][dt] = vfrag(st + 1, dt);
+        }
         bf16x8 pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -282,20 +412,13 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
           pf[e] = static_cast<__bf16>(p);
         }
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const int r1 = (tt * 32 + 16 * h) * D + voff[dt];
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&Vl[r1]));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&Vl[r1 + 8 * D]));
-          const bf16x8 va = __builtin_bit_cast(
-              bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){
-                          lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf, oacc[dt], 0, 0, 0);
-        }
+        for (int dt = 0; dt < D / 32; ++dt)
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st & 1][dt], pf, oacc[dt], 0, 0, 0);
       }
     }
     if (more) {
       __syncthreads();  // every wave is done with V
-      dma_block<D, BT, NW, true>(Vl, vp, len, wave, lane);
+      dma_block<D, BT, NW, true>(Vl, vp, len, wave, lane, vdma);
       PBSA_WAIT_VM(IPW);  // the next K has landed
       __syncthreads();
     }
