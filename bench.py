@@ -148,6 +148,50 @@ def train_step(torch, steps=5, warmup=2, device="cuda"):
             "bwd_flop_convention": "10*d per attended (row, token) pair, QK^T recompute included"}
 
 
+def rollout_bench(n_chunks, config_id, torch, n_layers=30, device="cuda"):
+    """Streaming rollout in the Wan shape: n_chunks chunks of 4680 tokens,
+    30 layers with independent state, window of the two previous chunks,
+    pool capped at 64 blocks, Top-C update after every chunk.  Each new chunk
+    plants 8 salient blocks along a direction re-drawn every 8 chunks.
+    Per-chunk latency = HIP events around the 30 layers' PBSA work on the
+    critical-path stream (inputs are generated on the device between
+    chunks, outside the events)."""
+    import pbsa_synth as syn
+    from block_sparse_attention_20_amd.rollout import Rollout, attended_tokens
+    s = syn.WAN_CHUNK
+    C = syn.ROLLOUT_POOL_CAP
+    shape = syn.Shape(B=s.B, H=s.H, d=s.d, T=s.T, Nq=s.Nq, W=0, C=C, topk=s.topk)
+    ro = Rollout(n_layers, s.B, s.H, s.d, s.T, s.Nq, C, s.topk, window_chunks=2, device=device,
+                 overlap=True)
+    sigma = 1 / math.sqrt(s.d)
+    ms, gflop, pool = [], [], []
+    for t in range(n_chunks):
+        for l in range(n_layers):
+            u = syn.rollout_direction(config_id, l, t, s.d, device=device)
+            ch = syn.make_chunk(shape, syn.rollout_seed(config_id, l, t), u, sigma=sigma, shift=1.5,
+                                n_planted=8, device=device)
+            ro.set_inputs(l, ch["q"], ch["k"], ch["v"])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for l in range(n_layers):
+            ro.run_layer(l)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+        gflop.append(sum(4 * s.d * attended_tokens(L) for L in ro.layers) / 1e9)
+        pool.append(int(ro.layers[0].t["pool_count"][0, 0].item()))
+        ro.advance()
+    steady = ms[4:]
+    med = sorted(steady)[len(steady) // 2]
+    return {"workload": f"streaming rollout, {n_chunks} chunks x {n_layers} layers, pool cap {C}",
+            "per_chunk_ms": [round(x, 3) for x in ms],
+            "per_chunk_gflop": [round(x, 1) for x in gflop],
+            "pool_blocks_after_update": pool,
+            "steady_median_ms": round(med, 3),
+            "steady_flatness": round((max(steady) - min(steady)) / med, 4),
+            "steady_tflops": round(sum(gflop[4:]) / sum(steady), 2)}
+
+
 def cpu_baseline(ro, budget_s, torch):
     """The fp64 oracle (as it stands) on a bounded sample of the same
     workload: layer 0's select over every head, then the forward of as many
@@ -199,6 +243,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle forward work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-train", action="store_true")
+    ap.add_argument("--no-rollout", action="store_true", help="skip the 20 s / 1 min rollouts")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: PBSA shards by head with no exchange, and this build "
@@ -247,6 +292,11 @@ def main():
     if not args.no_train:
         log("training step")
         out["train"] = train_step(torch)
+    if not args.no_rollout:
+        log("rollout 27 chunks (20 s)")
+        out["rollout_20s"] = rollout_bench(27, 2, torch)
+        log("rollout 80 chunks (1 min)")
+        out["rollout_1min"] = rollout_bench(80, 3, torch)
     if not args.no_cpu_baseline:
         log("cpu baseline")
         out["cpu_baseline"] = cpu_baseline(ro, args.cpu_budget, torch)

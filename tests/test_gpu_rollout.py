@@ -146,3 +146,55 @@ def test_rollout_work_is_flat_once_pool_full():
     assert pools[:4] == [[[0, 0]]] * 3 + [[[qb, qb]]]
     assert all(p == [[5, 5]] for p in pools[4:])
     assert sels[0] == 0 and all(s == 2 * qb * 2 for s in sels[1:])
+
+
+def test_rollout_wan_shape_teacher_forced():
+    """One layer of the 20 s rollout at its real shape (12 heads, 4680-token
+    chunks, pool cap 64, top-16) for 10 chunks: the pool fills at chunks 2-3
+    and the salient direction is re-drawn at chunk 8.  Each chunk: the GPU's
+    pool state equals the oracle's (teacher-forced on the GPU's selection and
+    masses), the oracle's own top-k agrees outside the 1e-4 tie band, and
+    sampled attention rows match."""
+    s = syn.WAN_CHUNK
+    C = syn.ROLLOUT_POOL_CAP
+    shape = syn.Shape(B=1, H=12, d=128, T=128, Nq=4680, W=0, C=C, topk=16)
+    ro = Rollout(1, 1, 12, 128, 128, 4680, C, 16)
+    orc = OracleRollout(1, 12, 128, 128, 4680, C, 16, 1 / math.sqrt(128))
+    L = ro.layers[0]
+    for t in range(10):
+        u = syn.rollout_direction(2, 0, t, 128)
+        ch = syn.make_chunk(shape, syn.rollout_seed(2, 0, t), u, sigma=1 / math.sqrt(128), shift=1.5,
+                            n_planted=8)
+        ro.set_inputs(0, ch["q"].cuda(), ch["k"].cuda(), ch["v"].cuda())
+        L.select(); L.fwd()
+        torch.cuda.synchronize()
+        sel = L.t["sel"].cpu().numpy(); cnt = L.t["sel_count"].cpu().numpy()
+        mp = L.t["mass_pool"].cpu().numpy(); mw = L.t["mass_win"].cpu().numpy()
+        o = L.t["o"].float().cpu().numpy()
+        if t >= 2:
+            L.update(ro.leaving[t % 2])
+        L.append_window(ro.first_slot(t), t * ro.QB)
+        ro.advance()
+        torch.cuda.synchronize()
+        blocks = [(0, h, i) for h in (0, 7) for i in (0, 36)]
+        ref = orc.step(ch["q"], ch["k"], ch["v"], sel_override=sel, sel_count_override=cnt,
+                       mass_override=(mp, mw), attn_blocks=blocks)
+        # the oracle's own routing on the same state: same sets outside ties
+        rs = ref["select"]
+        for idx in np.ndindex(*cnt.shape):
+            g = set(int(w) for w in sel[idx][:cnt[idx]]); orr = set(int(w) for w in rs["sel"][idx][:rs["sel_count"][idx]])
+            if g != orr:
+                sw = rs["s_win"][idx]
+                kth = sorted([v for v in sw if not np.isnan(v)], reverse=True)[15]
+                for w in g ^ orr:
+                    assert abs(sw[w] - kth) <= 1e-4 * max(abs(sw[w]), abs(kth))
+        rows = np.concatenate([np.arange(0, 128), np.arange(36 * 128, 4680)])
+        for h in (0, 7):
+            err = np.abs(o[0, h, rows] - ref["attn"]["o"][0, h, rows]).max()
+            assert err <= 2e-2, (t, h, err)
+        np.testing.assert_array_equal(L.t["pool_count"].cpu().numpy(), orc.pool_count)
+        for h in range(12):
+            n = int(orc.pool_count[0, h])
+            np.testing.assert_array_equal(L.t["pool_id"][0, h, :n].cpu().numpy(), orc.pool_id[0, h, :n])
+        _log(f"  wan rollout chunk {t}: pool {int(orc.pool_count[0, 0])}")
+    assert int(orc.pool_count[0, 0]) == C
