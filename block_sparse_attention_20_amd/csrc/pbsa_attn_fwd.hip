@@ -31,6 +31,7 @@
 // fp32 path: plain vector FMA version of the same walk (small problems).
 #include "pbsa_common.h"
 #include "pbsa_internal.h"
+#include "pbsa_tiles.h"
 
 namespace pbsa {
 
@@ -102,93 +103,6 @@ __device__ __forceinline__ int clamp_counts(const FwdArgs &a, size_t bh, int i, 
   return n_pool + sc + a.QB;
 }
 
-// 256 bytes of zeros: the DMA source for rows past a block's valid length
-// (padding rows and the tail of the last current block), so that they land
-// in LDS as zeros without a register round trip.
-__device__ __attribute__((aligned(256))) uint32_t g_zero_rows[64];
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// s_waitcnt immediate: vmcnt <= n, expcnt and lgkmcnt unconstrained (gfx9 encoding)
-#define PBSA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14)))
-
-// LDS swizzles (gfx950 LDS: 64 banks of 4 bytes; a 16-byte read serves 16
-// lanes per cycle, an 8-byte read 32 lanes).  Rows are 16-byte chunks; the
-// physical chunk of logical chunk c in row r is c ^ swz(r).
-//  K (read as MFMA A rows: 16 consecutive rows, one chunk each):
-//    d = 128: r & 15 (16 distinct chunks); d = 64: (r >> 1) & 7 with two rows
-//    per 256-byte bank line.
-//  V (read with ds_read_b64_tr_b16: 4 consecutive rows x 64 bytes per 32
-//    lanes): d = 128: 4 (r & 3) moves each row's 64-byte group to its own
-//    quarter of the bank line; d = 64: 2 (r & 3).
-template <int D, bool V>
-__device__ __forceinline__ int lds_swz(int r) {
-  if constexpr (V) return D == 128 ? 4 * (r & 3) : 2 * (r & 3);
-  else return D == 128 ? (r & 15) : ((r >> 1) & 7);
-}
-
-// Stage one [BT][D] bf16 block (rows >= len read as zeros) into LDS,
-// swizzled as above.  Each wave moves IPW chunks of 1 KB with
-// global_load_lds_dwordx4 (lane l lands at base + 16 l), so the whole block
-// is in flight without touching VGPRs.  Instruction `it` of a wave covers
-// rows row0 + it*RPI + lane/CPR; every wave's first row is a multiple of 16,
-// so a lane's source offset within its row band repeats every 16/RPI
-// instructions: dma_lane_offsets() computes those few byte offsets once.
-template <int D, int BT, int NW>
-struct DmaGeom {
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
-  static constexpr int RPI = 64 / CPR;          // rows per 1 KB instruction
-  static constexpr int IPW = BT * D * 2 / 1024 / NW;
-  static constexpr int NVAR = 16 / RPI < IPW ? 16 / RPI : IPW;  // distinct lane offsets
-  static_assert((IPW * RPI) % 16 == 0, "wave row ranges must start at multiples of 16");
-};
-
-template <int D, int BT, int NW, bool VSWZ>
-__device__ __forceinline__ void dma_lane_offsets(int lane, uint32_t (&ofs)[DmaGeom<D, BT, NW>::NVAR]) {
-  using G = DmaGeom<D, BT, NW>;
-  const int p = lane % G::CPR, rsub = lane / G::CPR;
-#pragma unroll
-  for (int v = 0; v < G::NVAR; ++v) {
-    const int rl = v * G::RPI + rsub;
-    ofs[v] = (uint32_t)((rl * D + (p ^ lds_swz<D, VSWZ>(rl)) * 8) * 2);
-  }
-}
-
-// Ragged block (len < BT): rows past len come from the zero page.
-template <int D, int BT, int NW>
-__device__ __forceinline__ void dma_block_ragged(uint16_t *dst, const char *base, int row0,
-                                                          int len, int lane,
-                                                          const uint32_t *ofs) {
-  using G = DmaGeom<D, BT, NW>;
-  const int rsub = lane / G::CPR, p = lane % G::CPR;
-#pragma unroll
-  for (int it = 0; it < G::IPW; ++it) {
-    const bool ok = row0 + it * G::RPI + rsub < len;
-    const char *g = ok ? base + (it / G::NVAR) * (G::NVAR * G::RPI * D * 2) + ofs[it % G::NVAR]
-                       : reinterpret_cast<const char *>(g_zero_rows + p * 4);
-    __builtin_amdgcn_global_load_lds(g, (lds_void *)(dst + it * 512), 16, 0, 0);
-  }
-}
-
-template <int D, int BT, int NW, bool VSWZ>
-__device__ __forceinline__ void dma_block(uint16_t *lds, const uint16_t *src, int len, int wave,
-                                          int lane, const uint32_t (&ofs)[DmaGeom<D, BT, NW>::NVAR]) {
-  using G = DmaGeom<D, BT, NW>;
-  const int row0 = wave * G::IPW * G::RPI;
-  const char *base = reinterpret_cast<const char *>(src + (size_t)row0 * D);
-  uint16_t *dst = lds + wave * G::IPW * 512;
-  if (len >= BT) {
-#pragma unroll
-    for (int it = 0; it < G::IPW; ++it) {
-      const char *g = base + (it / G::NVAR) * (G::NVAR * G::RPI * D * 2) + ofs[it % G::NVAR];
-      __builtin_amdgcn_global_load_lds(g, (lds_void *)(dst + it * 512), 16, 0, 0);
-    }
-  } else {
-    dma_block_ragged<D, BT, NW>(dst, base, row0, len, lane, ofs);
-  }
-}
-
 // The pool and selected-window part of a query block's list, resolved once
 // per workgroup into LDS: element offset of the block in its region and
 // (len | window << 16).  Entries past kMaxList fall back to resolve_block.
@@ -251,13 +165,21 @@ __device__ __forceinline__ void list_block(const FwdArgs &a, const BlockList &bl
   }
 }
 
+// K/V move through LDS in tiles of 64 tokens (a 128-token block is two
+// tiles; a block with <= 64 valid tokens is one), double buffered: the next
+// tile's DMA is issued as soon as the barrier at the top of a tile has
+// released the buffer of the previous one, so a whole tile of compute hides
+// it, with a single barrier per tile.  Four 16 KB buffers keep two
+// workgroups per CU.
+constexpr int kTile = 64;
+
 template <int D, int BT>
-__global__ __launch_bounds__(2 * BT, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
-  constexpr int NW = BT / 32;               // waves; wave w owns query rows [32w, 32w+32)
-  constexpr int CPR = D / 8;
-  constexpr int IPW = BT * D * 2 / 1024 / NW;
-  __shared__ __attribute__((aligned(1024))) uint16_t Kl[BT * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vl[BT * D];
+__global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kernel(FwdArgs a) {
+  constexpr int NW = BT / 32;  // waves; wave w owns query rows [32w, 32w+32)
+  constexpr int TT = kTile;
+  using G = DmaGeom<D, TT, NW>;
+  __shared__ __attribute__((aligned(1024))) uint16_t Kb[2][TT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vb[2][TT * D];
   __shared__ BlockList blist;
 
   int item;
@@ -292,82 +214,96 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   float m = -INFINITY, l = 0.f;  // running max (log2 units) and row sum
   const float sl2 = a.sl2;
 
-  // Per-lane LDS element offsets, fixed for the whole kernel (the swizzle of
-  // a row depends only on row & 7, which is fixed by the lane).
-  // K fragment (A of S^T): row tt*32 + l32, logical chunk 2kk + g.
+  // Per-lane LDS element offsets, fixed for the whole kernel.
+  // K fragment (A of S^T): tile row tt*32 + l32, logical chunk 2kk + g.
   int koff[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = l32 * D + (((2 * kk + g) ^ lds_swz<D, false>(l32)) * 8);
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = l32 * D + (((2 * kk + g) ^ lds_swz<D, kSwzK>(l32)) * 8);
   // V^T fragment via ds_read_b64_tr_b16: in each 16-lane group, lane gi
-  // addresses row gi/4 of a 4-row band (rows tt*32 + 16h + 4g + gi/4, and the
+  // addresses row gi/4 of a 4-row band (rows 16*step + 4g + gi/4, and the
   // band 8 rows further) and 4 of the group's 16 dims; it receives dim gi of
   // the 4 rows.
   const int gi = lane & 15, q16 = (lane >> 4) & 1;
   const int vr = gi >> 2, vq = gi & 3;
-  const int vsw = lds_swz<D, true>(4 * g + vr);  // rows step*16 + 4g + vr (+8) share it
+  const int vsw = lds_swz<D, kSwzV>(4 * g + vr);
   int voff[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
     voff[dt] = (4 * g + vr) * D + (((4 * dt + 2 * q16 + (vq >> 1)) ^ vsw) * 8) + (vq & 1) * 4;
-
-  uint32_t kdma[DmaGeom<D, BT, NW>::NVAR], vdma[DmaGeom<D, BT, NW>::NVAR];
-  dma_lane_offsets<D, BT, NW, false>(lane, kdma);
-  dma_lane_offsets<D, BT, NW, true>(lane, vdma);
+  uint32_t kdma[G::NVAR], vdma[G::NVAR];
+  dma_lane_offsets<D, TT, NW, kSwzK>(lane, kdma);
+  dma_lane_offsets<D, TT, NW, kSwzV>(lane, vdma);
   preload_list<D, BT>(a, bh, i, n_pool, sc, blist, t);
   __syncthreads();
-  const uint16_t *kp, *vp;
-  int len;
-  list_block<D, BT>(a, blist, bh, i, n_pool, sc, 0, kp, vp, len);
-  dma_block<D, BT, NW, false>(Kl, kp, len, wave, lane, kdma);
-  dma_block<D, BT, NW, true>(Vl, vp, len, wave, lane, vdma);
-  PBSA_WAIT_VM(0);
-  __syncthreads();
 
-  for (int j = 0; j < nb; ++j) {
-    const int len_cur = len;
-    // ---- S^T[token][query] = K Q^T
-    f32x16 sacc[BT / 32];
+  // tile stream: (block j, half h); tile rows = min(64, len_j - 64 h)
+  int j = 0, h = 0;
+  const uint16_t *kb, *vb;
+  int blen;
+  list_block<D, BT>(a, blist, bh, i, n_pool, sc, 0, kb, vb, blen);
+  int tlen = min(TT, blen);
+  dma_block<D, TT, NW, kSwzK>(Kb[0], kb, tlen, wave, lane, kdma);
+  dma_block<D, TT, NW, kSwzV>(Vb[0], vb, tlen, wave, lane, vdma);
+  int buf = 0;
+
+  while (true) {
+    PBSA_WAIT_VM(0);  // this tile has landed (own loads) ...
+    __syncthreads();  // ... for every wave, and every wave is done with the other buffer
+    // next tile
+    int jn = j, hn = h + 1, nlen = 0;
+    const uint16_t *kn = kb, *vn = vb;
+    int bn = blen;
+    if (hn * TT >= blen || hn * TT >= BT) {
+      jn = j + 1;
+      hn = 0;
+      if (jn < nb) list_block<D, BT>(a, blist, bh, i, n_pool, sc, jn, kn, vn, bn);
+    }
+    const bool more = jn < nb;
+    if (more) {
+      nlen = min(TT, bn - hn * TT);
+      dma_block<D, TT, NW, kSwzK>(Kb[buf ^ 1], kn + hn * TT * D, nlen, wave, lane, kdma);
+      dma_block<D, TT, NW, kSwzV>(Vb[buf ^ 1], vn + hn * TT * D, nlen, wave, lane, vdma);
+    }
+    const uint16_t *Kl = Kb[buf];
+    const uint16_t *Vl = Vb[buf];
+
+    // ---- S^T[token][query] = K Q^T over this tile's 64 tokens
+    f32x16 sacc[TT / 32];
 #pragma unroll
-    for (int tt = 0; tt < BT / 32; ++tt)
+    for (int tt = 0; tt < TT / 32; ++tt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[tt][e] = 0.f;
     {
-      bf16x8 ka[2][BT / 32];  // K fragments, one k-step ahead of the MFMAs
+      bf16x8 ka[2][TT / 32];  // K fragments, one k-step ahead of the MFMAs
 #pragma unroll
-      for (int tt = 0; tt < BT / 32; ++tt)
+      for (int tt = 0; tt < TT / 32; ++tt)
         ka[0][tt] = *reinterpret_cast<const bf16x8 *>(&Kl[tt * 32 * D + koff[0]]);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         if (kk + 1 < D / 16) {
 #pragma unroll
-          for (int tt = 0; tt < BT / 32; ++tt)
+          for (int tt = 0; tt < TT / 32; ++tt)
             ka[(kk + 1) & 1][tt] = *reinterpret_cast<const bf16x8 *>(&Kl[tt * 32 * D + koff[kk + 1]]);
         }
 #pragma unroll
-        for (int tt = 0; tt < BT / 32; ++tt)
+        for (int tt = 0; tt < TT / 32; ++tt)
           sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk & 1][tt], qf[kk], sacc[tt], 0, 0, 0);
       }
     }
-    __syncthreads();  // every wave is done with K
-    const bool more = j + 1 < nb;
-    if (more) {
-      list_block<D, BT>(a, blist, bh, i, n_pool, sc, j + 1, kp, vp, len);
-      dma_block<D, BT, NW, false>(Kl, kp, len, wave, lane, kdma);
-    }
     // ---- online softmax (log2 domain); the running max only moves when a
-    // block raises it by more than 8, so O is rarely rescaled and P <= 2^8.
-    if (len_cur < BT) {
+    // tile raises it by more than 8, so O is rarely rescaled and P <= 2^8.
+    if (tlen < TT) {
 #pragma unroll
-      for (int tt = 0; tt < BT / 32; ++tt)
+      for (int tt = 0; tt < TT / 32; ++tt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int tok = tt * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-          if (tok >= len_cur) sacc[tt][e] = -INFINITY;
+          if (tok >= tlen) sacc[tt][e] = -INFINITY;
         }
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int tt = 0; tt < BT / 32; ++tt)
+    for (int tt = 0; tt < TT / 32; ++tt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[tt][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
@@ -382,13 +318,10 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
         for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
     }
     const float muse = m == -INFINITY ? 0.f : m;
-    if (!more) PBSA_WAIT_VM(0);
-    else PBSA_WAIT_VM(IPW);  // V of this block has landed (K of the next may be in flight)
-    __syncthreads();
     // ---- O^T += V^T P^T  (V^T fragments read one step ahead)
     {
       auto vfrag = [&](int step, int dt) -> bf16x8 {
-        const int r1 = step * 16 * D + voff[dt];  // step = 2*tt + h
+        const int r1 = step * 16 * D + voff[dt];
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&Vl[r1]));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&Vl[r1 + 8 * D]));
         return __builtin_bit_cast(bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){
@@ -398,16 +331,16 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) va[0][dt] = vfrag(0, dt);
 #pragma unroll
-      for (int st = 0; st < BT / 16; ++st) {
-        const int tt = st >> 1, h = st & 1;
-        if (st + 1 < BT / 16) {
+      for (int st = 0; st < TT / 16; ++st) {
+        const int tt = st >> 1, hh = st & 1;
+        if (st + 1 < TT / 16) {
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt) va[(st + 1) & 1][dt] = vfrag(st + 1, dt);
         }
         bf16x8 pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(sacc[tt][8 * h + e] * sl2 - muse);
+          const float p = __builtin_amdgcn_exp2f(sacc[tt][8 * hh + e] * sl2 - muse);
           l += p;
           pf[e] = static_cast<__bf16>(p);
         }
@@ -416,12 +349,14 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st & 1][dt], pf, oacc[dt], 0, 0, 0);
       }
     }
-    if (more) {
-      __syncthreads();  // every wave is done with V
-      dma_block<D, BT, NW, true>(Vl, vp, len, wave, lane, vdma);
-      PBSA_WAIT_VM(IPW);  // the next K has landed
-      __syncthreads();
-    }
+    if (!more) break;
+    j = jn;
+    h = hn;
+    kb = kn;
+    vb = vn;
+    blen = bn;
+    tlen = nlen;
+    buf ^= 1;
   }
 
   // epilogue: O = O^T / l, LSE = ln(sum exp(scale s))
