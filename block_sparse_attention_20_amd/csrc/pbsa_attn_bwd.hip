@@ -11,20 +11,31 @@
 // D_r = <dO_r, O_r> and dS = P (dO V^T - D):
 //   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
 // Four launches:
-//   1. D = rowsum(dO * O) per query row;
+//   1. per query row: L = log2(e) lse and D, into arrays padded to whole
+//      query blocks (padding rows hold zeros);
 //   2. inverse selection lists: for every window slot, the query blocks that
-//      selected it (CSR, ascending query block, built per (b, h));
+//      selected it (CSR, ascending query block, built per (b, h) from the
+//      selection staged in LDS);
 //   3. dQ: one workgroup per (b, h, query block), walking the same block
-//      list as the forward (S^T, dP^T and dQ^T on MFMA; P and dS fed from
-//      the accumulators as B operands);
-//   4. dK/dV: one workgroup per stored KV block (pool slot, window slot,
-//      current block); it loops over the query blocks that attend it (all of
-//      them for pool and current blocks, the CSR list for window slots) and
-//      keeps its K/V in registers.  Blocks nobody attends get zeros.
+//      list as the forward; K and V tiles of 64 tokens are moved to LDS by
+//      DMA, double buffered.  S^T = K Q^T and dP^T = V dO^T take K and V rows
+//      as A operands; dQ^T += K^T dS^T reads K^T from the same tile with
+//      ds_read_b64_tr_b16.
+//   4. dK/dV: one workgroup per stored KV block (pool slot, current block,
+//      window slot - the ones attended by every query block first), looping
+//      over the query blocks that attend it (all of them for pool and current
+//      blocks, the CSR list for window slots) in 64-row Q/dO tiles, DMA
+//      staged and double buffered; K and V stay in registers.  Blocks nobody
+//      attends get zeros.
 // Every gradient element is written by exactly one workgroup, in a fixed
 // order, so results are bitwise reproducible.
+//
+// Tiles that are read both as rows (A operand, 16 lanes x 16 bytes per
+// cycle) and transposed (ds_read_b64_tr_b16, 4 rows x 64 bytes) use the
+// two-way swizzle kSwzU; tiles read only as rows use kSwzK.
 #include "pbsa_common.h"
 #include "pbsa_internal.h"
+#include "pbsa_tiles.h"
 
 namespace pbsa {
 
@@ -33,255 +44,315 @@ struct BwdArgs {
   const int32_t *win_len, *pool_len, *pool_count, *sel, *sel_count;
   const float *lse;
   uint16_t *dq, *dk_cur, *dv_cur, *dk_win, *dv_win, *dk_pool, *dv_pool;
-  float *Dv;
+  float *Lp, *Dp;  // [bh][QB*T]: log2(e) lse and D per query row, zero padded
   int32_t *qptr, *qidx;
   int32_t *status;
-  int H, Nq, W, C, topk, QB, n_items;
+  int H, Nq, W, C, topk, QB, n_items, per_xcd;
   float scale, sl2;
 };
 
-__device__ __forceinline__ int perm4b(int rg) { return (rg & ~3) | ((rg & 1) << 1) | ((rg >> 1) & 1); }
+constexpr int kTileB = 64;  // rows of every staged tile
 
-// rows [ROWS][D] -> LDS, row stride D+8, rows >= len zero
-template <int D, int ROWS, int NT>
-__device__ __forceinline__ void stage_rows(uint16_t *lds, const uint16_t *src, int len, int t) {
-  constexpr int CH = ROWS * D / 8;
-#pragma unroll
-  for (int c = t; c < CH; c += NT) {
-    const int row = c / (D / 8), col = c % (D / 8);
-    u32x4 v = {0, 0, 0, 0};
-    if (row < len) v = *reinterpret_cast<const u32x4 *>(src + row * D + col * 8);
-    *reinterpret_cast<u32x4 *>(lds + row * (D + 8) + col * 8) = v;
-  }
-}
-
-// rows [ROWS][D] -> LDS transposed [D][ROWS+8]; within every 16 rows the
-// 4-row groups 1 and 2 swap places, so that the rows one MFMA lane needs
-// (the accumulator layout of a 32x32 tile) are 8 contiguous elements.
-template <int D, int ROWS, int NT>
-__device__ __forceinline__ void stage_cols(uint16_t *lds, const uint16_t *src, int len, int t) {
-  constexpr int UN = (ROWS / 4) * (D / 8);
-  constexpr int VS = ROWS + 8;
-#pragma unroll
-  for (int u = t; u < UN; u += NT) {
-    const int rg = u % (ROWS / 4), dg = u / (ROWS / 4);
-    u32x4 v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = rg * 4 + e;
-      v[e] = u32x4{0, 0, 0, 0};
-      if (row < len) v[e] = *reinterpret_cast<const u32x4 *>(src + row * D + dg * 8);
-    }
-    uint16_t *dst = lds + (dg * 8) * VS + perm4b(rg) * 4;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int wd = c >> 1;
-      u32x2 pk;
-      if (c & 1) {
-        pk[0] = (v[0][wd] >> 16) | (v[1][wd] & 0xffff0000u);
-        pk[1] = (v[2][wd] >> 16) | (v[3][wd] & 0xffff0000u);
-      } else {
-        pk[0] = (v[0][wd] & 0xffffu) | (v[1][wd] << 16);
-        pk[1] = (v[2][wd] & 0xffffu) | (v[3][wd] << 16);
-      }
-      *reinterpret_cast<u32x2 *>(dst + c * VS) = pk;
-    }
-  }
+// consecutive items on the same XCD (workgroup n runs on XCD n % 8)
+__device__ __forceinline__ int bwd_item(const BwdArgs &a) {
+  return (blockIdx.x & 7) * a.per_xcd + (blockIdx.x >> 3);
 }
 
 // ---------------------------------------------------------------------------
-// 1. D_r = <dO_r, O_r>.  grid (ceil(rows/16)), 256 threads, 16 rows per block
+// 1. L_r = log2(e) lse_r and D_r = <dO_r, O_r>.  grid (ceil(bh*QB*T / rows
+//    per block)), 256 threads; rows past Nq of each (b, h) get zeros.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t *__restrict__ o,
-                                                         const uint16_t *__restrict__ dout,
-                                                         float *__restrict__ Dv, size_t rows) {
+__global__ __launch_bounds__(256) void bwd_rows_kernel(const uint16_t *__restrict__ o,
+                                                       const uint16_t *__restrict__ dout,
+                                                       const float *__restrict__ lse,
+                                                       float *__restrict__ Lp,
+                                                       float *__restrict__ Dp, size_t rows_p,
+                                                       int Nq, int NqP) {
   constexpr int TPR = D / 8;  // threads per row
-  const size_t r = (size_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const size_t rp = (size_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   const int c = threadIdx.x % TPR;
+  const size_t bh = rp / NqP;
+  const int r = (int)(rp % NqP);
+  const bool ok = rp < rows_p && r < Nq;
+  const size_t src = bh * Nq + r;
   float acc = 0.f;
-  if (r < rows) {
-    const u32x4 a = *reinterpret_cast<const u32x4 *>(o + r * D + c * 8);
-    const u32x4 b = *reinterpret_cast<const u32x4 *>(dout + r * D + c * 8);
+  if (ok) {
+    const u32x4 x = *reinterpret_cast<const u32x4 *>(o + src * D + c * 8);
+    const u32x4 y = *reinterpret_cast<const u32x4 *>(dout + src * D + c * 8);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc += bflo(a[e]) * bflo(b[e]) + bfhi(a[e]) * bfhi(b[e]);
+    for (int e = 0; e < 4; ++e) acc += bflo(x[e]) * bflo(y[e]) + bfhi(x[e]) * bfhi(y[e]);
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (r < rows && c == 0) Dv[r] = acc;
+  if (rp < rows_p && c == 0) {
+    Dp[rp] = acc;
+    Lp[rp] = ok ? lse[src] * kLog2e : 0.f;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// 2. inverse selection lists.  grid (H, B), 256 threads.
+// 2. inverse selection lists.  grid (H, B), 256 threads; thread t owns the
+//    window slots t, t + 256, t + 512, t + 768.  The selection rows are
+//    staged in LDS (invalid entries -1) and scanned in order, so each slot's
+//    list is in ascending query block order.
 // ---------------------------------------------------------------------------
+constexpr int kCsrChunk = 8192;
+
+__device__ __forceinline__ void csr_stage(int32_t *sl, const int32_t *sb, const int32_t *cb,
+                                          int base, int m, int topk, int W, int t) {
+  for (int e = t; e < m; e += 256) {
+    const int idx = base + e;
+    const int i = idx / topk, s = idx - i * topk;
+    const int w = s < cb[i] ? sb[idx] : -1;
+    sl[e] = w >= 0 && w < W ? w : -1;  // out-of-range slots select nothing
+  }
+}
+
 __global__ __launch_bounds__(256) void bwd_csr_kernel(const int32_t *__restrict__ sel,
                                                       const int32_t *__restrict__ sel_count,
                                                       int32_t *__restrict__ qptr,
                                                       int32_t *__restrict__ qidx, int H, int W,
                                                       int QB, int topk) {
-  __shared__ int32_t cnt[1025];
+  __shared__ int32_t sl[kCsrChunk];
+  __shared__ int32_t start[1024 + 1];
+  __shared__ int32_t wsum[4];
   const size_t bh = (size_t)blockIdx.y * H + blockIdx.x;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int32_t *sb = sel + bh * QB * (size_t)topk;
   const int32_t *cb = sel_count + bh * QB;
-  for (int w = t; w < W; w += 256) {
-    int n = 0;
-    for (int i = 0; i < QB; ++i) {
-      const int sc = max(0, min(cb[i], topk));
-      for (int s = 0; s < sc; ++s) n += sb[(size_t)i * topk + s] == w;
+  const int n = QB * topk;
+  int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+  for (int base = 0; base < n; base += kCsrChunk) {
+    const int m = min(kCsrChunk, n - base);
+    __syncthreads();
+    csr_stage(sl, sb, cb, base, m, topk, W, t);
+    __syncthreads();
+    for (int e = 0; e < m; ++e) {
+      const int w = sl[e];
+      c0 += w == t;
+      c1 += w == t + 256;
+      c2 += w == t + 512;
+      c3 += w == t + 768;
     }
-    cnt[w] = n;
   }
+  // exclusive scan over slots: thread t sums slots 4t..4t+3
   __syncthreads();
-  if (t == 0) {
-    int run = 0;
-    for (int w = 0; w < W; ++w) {
-      const int n = cnt[w];
-      cnt[w] = run;
-      run += n;
-    }
-    cnt[W] = run;
+  start[t] = c0;
+  start[t + 256] = c1;
+  start[t + 512] = c2;
+  start[t + 768] = c3;
+  __syncthreads();
+  int v[4], s = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[k] = 4 * t + k < W ? start[4 * t + k] : 0;
+    s += v[k];
   }
+  int incl = s;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int run = incl - s;
+  for (int w2 = 0; w2 < wave; ++w2) run += wsum[w2];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    start[4 * t + k] = run;
+    run += v[k];
+  }
+  if (t == 255) start[1024] = run;
   __syncthreads();
   int32_t *qp = qptr + bh * (W + 1);
+  for (int w = t; w < W; w += 256) qp[w] = start[w];
+  if (t == 0) qp[W] = start[W];
+  int p0 = start[t], p1 = start[t + 256], p2 = start[t + 512], p3 = start[t + 768];
   int32_t *qi = qidx + bh * QB * (size_t)topk;
-  for (int w = t; w <= W; w += 256) qp[w] = cnt[w];
-  for (int w = t; w < W; w += 256) {
-    int pos = cnt[w];
-    for (int i = 0; i < QB; ++i) {
-      const int sc = max(0, min(cb[i], topk));
-      for (int s = 0; s < sc; ++s)
-        if (sb[(size_t)i * topk + s] == w) qi[pos++] = i;
+  for (int base = 0; base < n; base += kCsrChunk) {
+    const int m = min(kCsrChunk, n - base);
+    __syncthreads();
+    csr_stage(sl, sb, cb, base, m, topk, W, t);
+    __syncthreads();
+    for (int e = 0; e < m; ++e) {
+      const int w = sl[e];
+      if (w < 0 || (w & 255) != t) continue;  // w < W <= 1024 here
+      const int i = (base + e) / topk;
+      const int k = w >> 8;
+      const int pos = k == 0 ? p0++ : k == 1 ? p1++ : k == 2 ? p2++ : p3++;
+      qi[pos] = i;
     }
   }
 }
 
-// block j of query block i's list (as the forward)
-template <int D, int BT>
-__device__ __forceinline__ void bwd_resolve(const BwdArgs &a, size_t bh, int i, int n_pool, int sc,
-                                            int j, const uint16_t *&kp, const uint16_t *&vp,
-                                            int &len) {
-  if (j < n_pool) {
-    const size_t off = (bh * a.C + j) * (size_t)(BT * D);
-    kp = a.k_pool + off;
-    vp = a.v_pool + off;
-    len = a.pool_len[bh * a.C + j];
-  } else if (j < n_pool + sc) {
-    const int w = a.sel[(bh * a.QB + i) * (size_t)a.topk + (j - n_pool)];
-    if (w < 0 || w >= a.W) {
-      set_status(a.status, PBSA_STATUS_SEL);
-      kp = a.k_win;
-      vp = a.v_win;
-      len = 0;
-      return;
-    }
-    const size_t off = (bh * a.W + w) * (size_t)(BT * D);
-    kp = a.k_win + off;
-    vp = a.v_win + off;
-    len = a.win_len[w];
-  } else {
-    const int c = j - n_pool - sc;
-    const size_t off = (bh * a.Nq + (size_t)c * BT) * D;
-    kp = a.k_cur + off;
-    vp = a.v_cur + off;
-    len = min(BT, a.Nq - c * BT);
+// Element offsets of the transposed (tr16) A fragments of a 32x32x16 MFMA
+// over a [64][D] tile swizzled with kSwzU: for 16 tile rows starting at a
+// multiple of 16, lane (gi = lane & 15) of each 16-lane group addresses row
+// 4g + gi/4 (lo) and the row 8 further (hi), dims 32 dt + 16 q16 + 4 (gi & 3).
+template <int D>
+__device__ __forceinline__ void tr_offsets(int lane, int (&lo)[D / 32], int (&hi)[D / 32]) {
+  const int g = lane >> 5, gi = lane & 15, q16 = (lane >> 4) & 1, vr = gi >> 2, vq = gi & 3;
+  const int rlo = 4 * g + vr, rhi = rlo + 8;
+  const int slo = lds_swz<D, kSwzU>(rlo), shi = lds_swz<D, kSwzU>(rhi);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int c = 4 * dt + 2 * q16 + (vq >> 1);
+    lo[dt] = rlo * D + ((c ^ slo) * 8) + (vq & 1) * 4;
+    hi[dt] = rhi * D + ((c ^ shi) * 8) + (vq & 1) * 4;
   }
-  len = max(0, min(len, BT));
 }
 
-__device__ __forceinline__ int bwd_item(const BwdArgs &a) {
-  const int per = (a.n_items + 7) / 8;
-  return (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+__device__ __forceinline__ bf16x8 tr_read(const uint16_t *tile, int lo, int hi) {
+  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&tile[lo]));
+  const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&tile[hi]));
+  return __builtin_bit_cast(bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){
+                                        x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]});
+}
+
+// this lane's row as MFMA B fragments (dims 16 kk + 8 g .. + 7)
+template <int D>
+__device__ __forceinline__ void load_bfrag(bf16x8 (&f)[D / 16], const uint16_t *row, bool ok, int g) {
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    u32x4 v = {0, 0, 0, 0};
+    if (ok) v = *reinterpret_cast<const u32x4 *>(row + kk * 16 + g * 8);
+    f[kk] = __builtin_bit_cast(bf16x8, v);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // 3. dQ per (b, h, query block).
 // ---------------------------------------------------------------------------
 template <int D, int BT>
-__global__ __launch_bounds__(2 * BT) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int NT = 2 * BT;
-  constexpr int KS = D + 8, TS = BT + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BT * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BT * KS];
+__global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int NW = BT / 32, TT = kTileB;
+  using G = DmaGeom<D, TT, NW>;
+  __shared__ __attribute__((aligned(1024))) uint16_t Kb[2][TT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vb[2][TT * D];
+  __shared__ BlockList blist;
   const int item = bwd_item(a);
   if (item >= a.n_items) return;
   const int i = item % a.QB;
   const size_t bh = item / a.QB;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, g = lane >> 5;
-  int n_pool = max(0, min(a.pool_count[bh], a.C));
-  int sc = max(0, min(a.sel_count[bh * a.QB + i], a.topk));
-  const int nb = n_pool + sc + a.QB;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  int n_pool, sc;
+  const int nb = clamp_counts(a, bh, i, n_pool, sc);
+
+  // this lane's query column: Q and dO rows as B fragments
   const int qrow = i * BT + wave * 32 + l32;
   const bool qok = qrow < a.Nq;
   bf16x8 qf[D / 16], df[D / 16];
   {
     const size_t base = (bh * a.Nq + (qok ? qrow : 0)) * (size_t)D;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4 v = {0, 0, 0, 0}, w = {0, 0, 0, 0};
-      if (qok) {
-        v = *reinterpret_cast<const u32x4 *>(a.q + base + kk * 16 + g * 8);
-        w = *reinterpret_cast<const u32x4 *>(a.dout + base + kk * 16 + g * 8);
-      }
-      qf[kk] = __builtin_bit_cast(bf16x8, v);
-      df[kk] = __builtin_bit_cast(bf16x8, w);
-    }
+    load_bfrag<D>(qf, a.q + base, qok, g);
+    load_bfrag<D>(df, a.dout + base, qok, g);
   }
-  const float lse2 = qok ? a.lse[bh * a.Nq + qrow] * kLog2e : INFINITY;
-  const float Dq = qok ? a.Dv[bh * a.Nq + qrow] : 0.f;
+  const size_t prow = bh * (size_t)(a.QB * BT) + qrow;
+  const float Lq = a.Lp[prow];
+  const float Dq = a.Dp[prow];
+  const float sl2 = a.sl2;
   f32x16 dqacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) dqacc[dt][e] = 0.f;
 
-  for (int j = 0; j < nb; ++j) {
-    const uint16_t *kp, *vp;
-    int len;
-    bwd_resolve<D, BT>(a, bh, i, n_pool, sc, j, kp, vp, len);
+  // A = K / V rows: tile row 32 half + l32, logical chunk 2 kk + g
+  int koff[D / 16], voff[D / 16];
+  {
+    const int ks = lds_swz<D, kSwzU>(l32), vs = lds_swz<D, kSwzK>(l32);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      koff[kk] = l32 * D + (((2 * kk + g) ^ ks) * 8);
+      voff[kk] = l32 * D + (((2 * kk + g) ^ vs) * 8);
+    }
+  }
+  int tlo[D / 32], thi[D / 32];
+  tr_offsets<D>(lane, tlo, thi);
+  uint32_t kdma[G::NVAR], vdma[G::NVAR];
+  dma_lane_offsets<D, TT, NW, kSwzU>(lane, kdma);
+  dma_lane_offsets<D, TT, NW, kSwzK>(lane, vdma);
+  preload_list<D, BT>(a, bh, i, n_pool, sc, blist, t, 2 * BT);
+  __syncthreads();
+
+  int j = 0, h = 0;
+  const uint16_t *kb, *vb;
+  int blen;
+  list_block<D, BT>(a, blist, bh, i, n_pool, sc, 0, kb, vb, blen);
+  int tlen = min(TT, blen);
+  dma_block<D, TT, NW, kSwzU>(Kb[0], kb, tlen, wave, lane, kdma);
+  dma_block<D, TT, NW, kSwzK>(Vb[0], vb, tlen, wave, lane, vdma);
+  int buf = 0;
+
+  while (true) {
+    PBSA_WAIT_VM(0);
     __syncthreads();
-    stage_rows<D, BT, NT>(Ks, kp, len, t);
-    stage_cols<D, BT, NT>(Kt, kp, len, t);
-    stage_rows<D, BT, NT>(Vs, vp, len, t);
-    __syncthreads();
-    f32x16 sacc[BT / 32], pacc[BT / 32];
+    int jn = j, hn = h + 1, nlen = 0;
+    const uint16_t *kn = kb, *vn = vb;
+    int bn = blen;
+    if (hn * TT >= blen || hn * TT >= BT) {
+      jn = j + 1;
+      hn = 0;
+      if (jn < nb) list_block<D, BT>(a, blist, bh, i, n_pool, sc, jn, kn, vn, bn);
+    }
+    const bool more = jn < nb;
+    if (more) {
+      nlen = min(TT, bn - hn * TT);
+      dma_block<D, TT, NW, kSwzU>(Kb[buf ^ 1], kn + hn * TT * D, nlen, wave, lane, kdma);
+      dma_block<D, TT, NW, kSwzK>(Vb[buf ^ 1], vn + hn * TT * D, nlen, wave, lane, vdma);
+    }
+    const uint16_t *Kl = Kb[buf];
+    const uint16_t *Vl = Vb[buf];
+
 #pragma unroll
-    for (int tt = 0; tt < BT / 32; ++tt)
+    for (int hf = 0; hf < TT / 32; ++hf) {
+      if (hf * 32 < tlen) {
+        // S^T = K Q^T and dP^T = V dO^T over 32 tokens
+        f32x16 sacc, pacc;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[tt][e] = pacc[tt][e] = 0.f;
+        for (int e = 0; e < 16; ++e) sacc[e] = pacc[e] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&Kl[hf * 32 * D + koff[kk]]);
+          const bf16x8 va = *reinterpret_cast<const bf16x8 *>(&Vl[hf * 32 * D + voff[kk]]);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[kk], pacc, 0, 0, 0);
+        }
+        // dS^T = P^T (dP^T - D); tokens past the tile's length are masked
+        const bool ragged = tlen < hf * 32 + 32;
 #pragma unroll
-      for (int tt = 0; tt < BT / 32; ++tt) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&Ks[(tt * 32 + l32) * KS + kk * 16 + g * 8]);
-        const bf16x8 va = *reinterpret_cast<const bf16x8 *>(&Vs[(tt * 32 + l32) * KS + kk * 16 + g * 8]);
-        sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc[tt], 0, 0, 0);
-        pacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[kk], pacc[tt], 0, 0, 0);
-      }
-    // dS^T = P^T (dP^T - D), padding tokens masked
+        for (int e = 0; e < 16; ++e) {
+          float p = __builtin_amdgcn_exp2f(sacc[e] * sl2 - Lq);
+          if (ragged && hf * 32 + 8 * (e >> 2) + 4 * g + (e & 3) >= tlen) p = 0.f;
+          sacc[e] = p * (pacc[e] - Dq);
+        }
+        // dQ^T += K^T dS^T, 16 tokens per step
 #pragma unroll
-    for (int tt = 0; tt < BT / 32; ++tt)
+        for (int hh = 0; hh < 2; ++hh) {
+          bf16x8 sf;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int tok = tt * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-        const float p = tok < len ? __builtin_amdgcn_exp2f(sacc[tt][e] * a.sl2 - lse2) : 0.f;
-        sacc[tt][e] = p * (pacc[tt][e] - Dq);
-      }
-    // dQ^T += K^T dS^T
+          for (int e = 0; e < 8; ++e) sf[e] = static_cast<__bf16>(sacc[8 * hh + e]);
+          const uint16_t *Kst = Kl + (2 * hf + hh) * 16 * D;
 #pragma unroll
-    for (int tt = 0; tt < BT / 32; ++tt)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        bf16x8 sf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sf[e] = static_cast<__bf16>(sacc[tt][8 * h + e]);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&Kt[(dt * 32 + l32) * TS + tt * 32 + h * 16 + g * 8]);
-          dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, sf, dqacc[dt], 0, 0, 0);
+          for (int dt = 0; dt < D / 32; ++dt)
+            dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(Kst, tlo[dt], thi[dt]), sf,
+                                                                dqacc[dt], 0, 0, 0);
         }
       }
+    }
+    if (!more) break;
+    j = jn;
+    h = hn;
+    kb = kn;
+    vb = vn;
+    blen = bn;
+    tlen = nlen;
+    buf ^= 1;
   }
   if (qok) {
     uint16_t *op = a.dq + (bh * a.Nq + qrow) * (size_t)D;
@@ -298,144 +369,207 @@ __global__ __launch_bounds__(2 * BT) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 4. dK, dV per stored KV block.  Items: [pool C | window W | current QB]
-//    per (b, h).
+// 4. dK, dV per stored KV block.  Items per (b, h):
+//    [pool C | current QB | window W].
 // ---------------------------------------------------------------------------
+
+// L and D of query rows [r0, r0 + 64) into LD[0..63] and LD[64..127] with one
+// 1 KB DMA by wave 0 (lanes 32..63 fill LD[128..255] from the zero page).
+__device__ __forceinline__ void dma_rows_ld(float *LD, const float *L, const float *Dv, int lane) {
+  const char *g = lane < 16   ? reinterpret_cast<const char *>(L + 4 * lane)
+                  : lane < 32 ? reinterpret_cast<const char *>(Dv + 4 * (lane - 16))
+                              : reinterpret_cast<const char *>(g_zero_rows + 4 * (lane & 15));
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)LD, 16, 0, 0);
+}
+
 template <int D, int BT>
-__global__ __launch_bounds__(2 * BT) void bwd_dkv_kernel(BwdArgs a) {
-  constexpr int NT = 2 * BT;
-  constexpr int KS = D + 8, TS = BT + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[BT * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t Os[BT * KS];  // dO rows
-  __shared__ __attribute__((aligned(16))) uint16_t Ot[D * TS];   // dO transposed
-  __shared__ float lse2s[BT], Ds[BT];
+__global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dkv_kernel(BwdArgs a) {
+  constexpr int NW = BT / 32, TT = kTileB;
+  using G = DmaGeom<D, TT, NW>;
+  __shared__ __attribute__((aligned(1024))) uint16_t Qb[2][TT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ob[2][TT * D];  // dO rows
+  __shared__ __attribute__((aligned(1024))) float LD[2][256];
   const int item = bwd_item(a);
   if (item >= a.n_items) return;
   const int nj = a.C + a.W + a.QB;
   const int jb = item % nj;
   const size_t bh = item / nj;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, g = lane >> 5;
-  const int n_pool = max(0, min(a.pool_count[bh], a.C));
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  int n_pool = a.pool_count[bh];
+  n_pool = max(0, min(n_pool, a.C));
 
-  const uint16_t *kp = nullptr, *vp = nullptr;
+  const uint16_t *kp, *vp;
   uint16_t *dkp, *dvp;
-  int len, nq = 0, list_base = 0;
-  bool all_q = false;
+  int len, nq, list_base = 0;
+  bool all_q = true, is_cur = false;
   if (jb < a.C) {
     const size_t off = (bh * a.C + jb) * (size_t)(BT * D);
     kp = a.k_pool + off; vp = a.v_pool + off; dkp = a.dk_pool + off; dvp = a.dv_pool + off;
     len = jb < n_pool ? max(0, min(a.pool_len[bh * a.C + jb], BT)) : 0;
-    all_q = true;
-  } else if (jb < a.C + a.W) {
-    const int w = jb - a.C;
+  } else if (jb < a.C + a.QB) {
+    const int c = jb - a.C;
+    const size_t off = (bh * a.Nq + (size_t)c * BT) * D;
+    kp = a.k_cur + off; vp = a.v_cur + off; dkp = a.dk_cur + off; dvp = a.dv_cur + off;
+    len = min(BT, a.Nq - c * BT);
+    is_cur = true;
+  } else {
+    const int w = jb - a.C - a.QB;
     const size_t off = (bh * a.W + w) * (size_t)(BT * D);
     kp = a.k_win + off; vp = a.v_win + off; dkp = a.dk_win + off; dvp = a.dv_win + off;
     len = max(0, min(a.win_len[w], BT));
     list_base = a.qptr[bh * (a.W + 1) + w];
     nq = a.qptr[bh * (a.W + 1) + w + 1] - list_base;
-  } else {
-    const int c = jb - a.C - a.W;
-    const size_t off = (bh * a.Nq + (size_t)c * BT) * D;
-    kp = a.k_cur + off; vp = a.v_cur + off; dkp = a.dk_cur + off; dvp = a.dv_cur + off;
-    len = min(BT, a.Nq - c * BT);
-    all_q = true;
+    all_q = false;
   }
-  if (all_q) nq = len > 0 ? a.QB : 0;
-  const bool is_cur = jb >= a.C + a.W;
+  if (all_q) nq = a.QB;
+  if (len == 0) nq = 0;
+  const int32_t *ql = a.qidx + bh * a.QB * (size_t)a.topk + list_base;
 
-  // this lane's key token, held as B fragments (K^T and V^T columns)
+  // this lane's key token: K and V rows as B fragments
   const int tok = wave * 32 + l32;
   const bool tok_ok = tok < len;
   bf16x8 kf[D / 16], vf[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    u32x4 v = {0, 0, 0, 0}, w = {0, 0, 0, 0};
-    if (tok_ok) {
-      v = *reinterpret_cast<const u32x4 *>(kp + tok * D + kk * 16 + g * 8);
-      w = *reinterpret_cast<const u32x4 *>(vp + tok * D + kk * 16 + g * 8);
-    }
-    kf[kk] = __builtin_bit_cast(bf16x8, v);
-    vf[kk] = __builtin_bit_cast(bf16x8, w);
-  }
+  load_bfrag<D>(kf, kp + (tok_ok ? tok : 0) * (size_t)D, tok_ok, g);
+  load_bfrag<D>(vf, vp + (tok_ok ? tok : 0) * (size_t)D, tok_ok, g);
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) dkacc[dt][e] = dvacc[dt][e] = 0.f;
+  const float sl2 = a.sl2;
 
-  for (int n = 0; n < nq; ++n) {
-    const int i = all_q ? n : a.qidx[bh * a.QB * (size_t)a.topk + list_base + n];
-    const int r0 = i * BT;
-    const int qlen = min(BT, a.Nq - r0);
-    const size_t roff = (bh * a.Nq + r0) * (size_t)D;
-    __syncthreads();
-    stage_rows<D, BT, NT>(Qs, a.q + roff, qlen, t);
-    stage_cols<D, BT, NT>(Qt, a.q + roff, qlen, t);
-    stage_rows<D, BT, NT>(Os, a.dout + roff, qlen, t);
-    stage_cols<D, BT, NT>(Ot, a.dout + roff, qlen, t);
-    for (int r = t; r < BT; r += NT) {
-      lse2s[r] = r < qlen ? a.lse[bh * a.Nq + r0 + r] * kLog2e : INFINITY;
-      Ds[r] = r < qlen ? a.Dv[bh * a.Nq + r0 + r] : 0.f;
+  if (nq > 0) {
+    // A = Q / dO rows: tile row 32 qs + l32, logical chunk 2 kk + g
+    // (chunk 2 kk + g) ^ s = (g ^ s) ^ 2 kk: one base offset, XOR 16 kk per step
+    const int rbase = l32 * D + ((g ^ lds_swz<D, kSwzU>(l32)) * 8);
+    int tlo[D / 32], thi[D / 32];
+    tr_offsets<D>(lane, tlo, thi);
+    uint32_t rdma[G::NVAR];
+    dma_lane_offsets<D, TT, NW, kSwzU>(lane, rdma);
+    const size_t NqP = (size_t)a.QB * BT;
+
+    // query tile stream: list entry n (query block qi), half h
+    int n = 0, h = 0;
+    int qi = all_q ? 0 : __builtin_amdgcn_readfirstlane(ql[0]);
+    int qlen = min(BT, a.Nq - qi * BT);
+    int tlen = min(TT, qlen);
+    {
+      const size_t r0 = bh * a.Nq + (size_t)qi * BT;
+      dma_block<D, TT, NW, kSwzU>(Qb[0], a.q + r0 * D, tlen, wave, lane, rdma);
+      dma_block<D, TT, NW, kSwzU>(Ob[0], a.dout + r0 * D, tlen, wave, lane, rdma);
+      if (wave == 0) dma_rows_ld(LD[0], a.Lp + bh * NqP + qi * BT, a.Dp + bh * NqP + qi * BT, lane);
     }
-    __syncthreads();
-    // S[q][tok] = Q K^T and dP[q][tok] = dO V^T
-    f32x16 sacc[BT / 32], pacc[BT / 32];
-#pragma unroll
-    for (int qt = 0; qt < BT / 32; ++qt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[qt][e] = pacc[qt][e] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-      for (int qt = 0; qt < BT / 32; ++qt) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(&Qs[(qt * 32 + l32) * KS + kk * 16 + g * 8]);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8 *>(&Os[(qt * 32 + l32) * KS + kk * 16 + g * 8]);
-        sacc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], sacc[qt], 0, 0, 0);
-        pacc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], pacc[qt], 0, 0, 0);
-      }
-    // P and dS (element (qt, e) is query row qt*32 + 8(e/4) + 4g + e%4)
-#pragma unroll
-    for (int qt = 0; qt < BT / 32; ++qt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int qr = qt * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-        const float p = tok_ok ? __builtin_amdgcn_exp2f(sacc[qt][e] * a.sl2 - lse2s[qr]) : 0.f;
-        sacc[qt][e] = p;
-        pacc[qt][e] = p * (pacc[qt][e] - Ds[qr]);
-      }
-    // dV^T += dO^T P ; dK^T += Q^T dS
-#pragma unroll
-    for (int qt = 0; qt < BT / 32; ++qt)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        bf16x8 pf, sf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pf[e] = static_cast<__bf16>(sacc[qt][8 * h + e]);
-          sf[e] = static_cast<__bf16>(pacc[qt][8 * h + e]);
-        }
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const int off = (dt * 32 + l32) * TS + qt * 32 + h * 16 + g * 8;
-          const bf16x8 oa = *reinterpret_cast<const bf16x8 *>(&Ot[off]);
-          const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(&Qt[off]);
-          dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pf, dvacc[dt], 0, 0, 0);
-          dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sf, dkacc[dt], 0, 0, 0);
+    int buf = 0;
+    while (true) {
+      PBSA_WAIT_VM(0);
+      __syncthreads();
+      int nn = n, hn = h + 1, qin = qi, qlenn = qlen, nlen = 0;
+      if (hn * TT >= qlen || hn * TT >= BT) {
+        nn = n + 1;
+        hn = 0;
+        if (nn < nq) {
+          qin = all_q ? nn : __builtin_amdgcn_readfirstlane(ql[nn]);
+          qlenn = min(BT, a.Nq - qin * BT);
         }
       }
+      const bool more = nn < nq;
+      if (more) {
+        nlen = min(TT, qlenn - hn * TT);
+        const size_t r0 = bh * a.Nq + (size_t)qin * BT + hn * TT;
+        dma_block<D, TT, NW, kSwzU>(Qb[buf ^ 1], a.q + r0 * D, nlen, wave, lane, rdma);
+        dma_block<D, TT, NW, kSwzU>(Ob[buf ^ 1], a.dout + r0 * D, nlen, wave, lane, rdma);
+        if (wave == 0) {
+          const size_t p0 = bh * NqP + (size_t)qin * BT + hn * TT;
+          dma_rows_ld(LD[buf ^ 1], a.Lp + p0, a.Dp + p0, lane);
+        }
+      }
+      const uint16_t *Ql = Qb[buf];
+      const uint16_t *Ol = Ob[buf];
+      const float *Ll = LD[buf];
+      const float *Dl = LD[buf] + 64;
+
+#pragma unroll 1
+      for (int qs = 0; qs < TT / 32; ++qs) {
+        if (qs * 32 < tlen) {
+          // S = Q K^T and dP = dO V^T over 32 query rows (element e of a
+          // lane is query row 32 qs + 8 (e / 4) + 4 g + e % 4)
+          f32x16 sacc, pacc;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sacc[e] = pacc[e] = 0.f;
+#pragma unroll
+          for (int kk = 0; kk < D / 16; ++kk) {
+            const int ro = qs * 32 * D + (rbase ^ (16 * kk));
+            const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(&Ql[ro]);
+            const bf16x8 oa = *reinterpret_cast<const bf16x8 *>(&Ol[ro]);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], sacc, 0, 0, 0);
+            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], pacc, 0, 0, 0);
+          }
+          // P and dS.  Rows past the query block are zero in Q, dO, L and D,
+          // so they contribute nothing (P = 1, dS = 0 there).
+#pragma unroll
+          for (int m4 = 0; m4 < 4; ++m4) {
+            const f32x4 L4 = *reinterpret_cast<const f32x4 *>(&Ll[qs * 32 + 8 * m4 + 4 * g]);
+            const f32x4 D4 = *reinterpret_cast<const f32x4 *>(&Dl[qs * 32 + 8 * m4 + 4 * g]);
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const int e = 4 * m4 + e4;
+              const float p = __builtin_amdgcn_exp2f(sacc[e] * sl2 - L4[e4]);
+              sacc[e] = p;
+              pacc[e] = p * (pacc[e] - D4[e4]);
+            }
+          }
+          // dV^T += dO^T P and dK^T += Q^T dS, 16 query rows per step
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            bf16x8 pf, sf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              pf[e] = static_cast<__bf16>(sacc[8 * hh + e]);
+              sf[e] = static_cast<__bf16>(pacc[8 * hh + e]);
+            }
+            const int st = (2 * qs + hh) * 16 * D;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+              dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(Ol + st, tlo[dt], thi[dt]), pf,
+                                                                  dvacc[dt], 0, 0, 0);
+              dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(Ql + st, tlo[dt], thi[dt]), sf,
+                                                                  dkacc[dt], 0, 0, 0);
+            }
+          }
+        }
+      }
+      if (!more) break;
+      n = nn;
+      h = hn;
+      qi = qin;
+      qlen = qlenn;
+      tlen = nlen;
+      buf ^= 1;
+    }
   }
-  // write this lane's token row (zeros for padding rows of stored slots)
+  // this lane's token row.  Padding rows of stored slots get zeros: their
+  // accumulator columns hold whatever P gave for zero K/V rows (possibly
+  // not finite), so they are replaced, not scaled.  Rows past Nq of the
+  // last current block do not exist.
   if (is_cur && !tok_ok) return;
+  if (!tok_ok) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dkacc[dt][e] = dvacc[dt][e] = 0.f;
+  }
   uint16_t *dk = dkp + tok * (size_t)D;
   uint16_t *dv = dvp + tok * (size_t)D;
+  const float ks = a.scale;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       u32x2 pk, pv;
-      pk[0] = pack_bf16x2(dkacc[dt][4 * jj] * a.scale, dkacc[dt][4 * jj + 1] * a.scale);
-      pk[1] = pack_bf16x2(dkacc[dt][4 * jj + 2] * a.scale, dkacc[dt][4 * jj + 3] * a.scale);
+      pk[0] = pack_bf16x2(dkacc[dt][4 * jj] * ks, dkacc[dt][4 * jj + 1] * ks);
+      pk[1] = pack_bf16x2(dkacc[dt][4 * jj + 2] * ks, dkacc[dt][4 * jj + 3] * ks);
       pv[0] = pack_bf16x2(dvacc[dt][4 * jj], dvacc[dt][4 * jj + 1]);
       pv[1] = pack_bf16x2(dvacc[dt][4 * jj + 2], dvacc[dt][4 * jj + 3]);
       *reinterpret_cast<u32x2 *>(dk + dt * 32 + 8 * jj + 4 * g) = pk;
@@ -446,7 +580,8 @@ __global__ __launch_bounds__(2 * BT) void bwd_dkv_kernel(BwdArgs a) {
 size_t bwd_ws_bytes(const pbsa_problem &p) {
   const size_t bh = (size_t)p.B * p.H;
   const size_t QB = (p.Nq + p.T - 1) / p.T;
-  return align256(bh * p.Nq * sizeof(float)) + align256(bh * (p.W + 1) * sizeof(int32_t)) +
+  const size_t rows_p = bh * QB * p.T;
+  return 2 * align256(rows_p * sizeof(float)) + align256(bh * (p.W + 1) * sizeof(int32_t)) +
          align256(bh * QB * (size_t)(p.topk > 0 ? p.topk : 1) * sizeof(int32_t));
 }
 
@@ -473,29 +608,36 @@ hipError_t launch_attn_bwd(const pbsa_problem &p, float scale, const void *q, co
   a.scale = scale;
   a.sl2 = scale * kLog2e;
   const size_t bh = (size_t)p.B * p.H;
+  const size_t rows_p = bh * a.QB * p.T;
   char *w = reinterpret_cast<char *>(ws);
-  a.Dv = reinterpret_cast<float *>(w);
-  w += align256(bh * p.Nq * sizeof(float));
+  a.Lp = reinterpret_cast<float *>(w);
+  w += align256(rows_p * sizeof(float));
+  a.Dp = reinterpret_cast<float *>(w);
+  w += align256(rows_p * sizeof(float));
   a.qptr = reinterpret_cast<int32_t *>(w);
   w += align256(bh * (p.W + 1) * sizeof(int32_t));
   a.qidx = reinterpret_cast<int32_t *>(w);
 
-  const size_t rows = bh * p.Nq;
-  const unsigned rblocks = (unsigned)((rows + (256 / (p.d / 8)) - 1) / (256 / (p.d / 8)));
+  const int rpb = 256 / (p.d / 8);
+  const unsigned rblocks = (unsigned)((rows_p + rpb - 1) / rpb);
+  const int NqP = a.QB * p.T;
   if (p.d == 128)
-    bwd_rowdot_kernel<128><<<rblocks, 256, 0, st>>>(a.o, a.dout, a.Dv, rows);
+    bwd_rows_kernel<128><<<rblocks, 256, 0, st>>>(a.o, a.dout, lse, a.Lp, a.Dp, rows_p, p.Nq, NqP);
   else
-    bwd_rowdot_kernel<64><<<rblocks, 256, 0, st>>>(a.o, a.dout, a.Dv, rows);
-  if (p.W > 0) bwd_csr_kernel<<<dim3(p.H, p.B), 256, 0, st>>>(sel, sel_count, a.qptr, a.qidx, p.H, p.W, a.QB, p.topk);
+    bwd_rows_kernel<64><<<rblocks, 256, 0, st>>>(a.o, a.dout, lse, a.Lp, a.Dp, rows_p, p.Nq, NqP);
+  if (p.W > 0 && p.topk > 0)
+    bwd_csr_kernel<<<dim3(p.H, p.B), 256, 0, st>>>(sel, sel_count, a.qptr, a.qidx, p.H, p.W, a.QB, p.topk);
 
   const dim3 block(2 * p.T);
-#define PBSA_BWD_CASE(D_, T_)                                               \
-  if (p.d == D_ && p.T == T_) {                                             \
-    a.n_items = (int)(bh * a.QB);                                           \
-    bwd_dq_kernel<D_, T_><<<dim3(8 * ((a.n_items + 7) / 8)), block, 0, st>>>(a); \
-    a.n_items = (int)(bh * (p.C + p.W + a.QB));                             \
-    bwd_dkv_kernel<D_, T_><<<dim3(8 * ((a.n_items + 7) / 8)), block, 0, st>>>(a); \
-    return hipGetLastError();                                               \
+#define PBSA_BWD_CASE(D_, T_)                                                     \
+  if (p.d == D_ && p.T == T_) {                                                   \
+    a.n_items = (int)(bh * a.QB);                                                 \
+    a.per_xcd = (a.n_items + 7) / 8;                                              \
+    bwd_dq_kernel<D_, T_><<<dim3(8 * a.per_xcd), block, 0, st>>>(a);              \
+    a.n_items = (int)(bh * (p.C + p.W + a.QB));                                   \
+    a.per_xcd = (a.n_items + 7) / 8;                                              \
+    bwd_dkv_kernel<D_, T_><<<dim3(8 * a.per_xcd), block, 0, st>>>(a);             \
+    return hipGetLastError();                                                     \
   }
   PBSA_BWD_CASE(128, 128)
   PBSA_BWD_CASE(64, 128)

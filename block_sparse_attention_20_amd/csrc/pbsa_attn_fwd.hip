@@ -45,124 +45,9 @@ struct FwdArgs {
   float sl2;  // scale * log2(e)
 };
 
-// Which stored block is entry j of query block i's attended list, and how
-// many of its rows are valid.  Order: pool slots, selected window slots,
-// current-chunk blocks.
-template <typename TIn, int D, int BT>
-__device__ __forceinline__ void resolve_block(const FwdArgs &a, size_t bh, int i, int n_pool,
-                                              int sc, int j, const TIn *&kp, const TIn *&vp,
-                                              int &len) {
-  if (j < n_pool) {
-    const size_t off = (bh * a.C + j) * (size_t)(BT * D);
-    kp = (const TIn *)a.k_pool + off;
-    vp = (const TIn *)a.v_pool + off;
-    len = a.pool_len[bh * a.C + j];
-  } else if (j < n_pool + sc) {
-    const int w = a.sel[(bh * a.QB + i) * (size_t)a.topk + (j - n_pool)];
-    if (w < 0 || w >= a.W) {
-      set_status(a.status, PBSA_STATUS_SEL);
-      kp = (const TIn *)a.k_win;
-      vp = (const TIn *)a.v_win;
-      len = 0;
-      return;
-    }
-    const size_t off = (bh * a.W + w) * (size_t)(BT * D);
-    kp = (const TIn *)a.k_win + off;
-    vp = (const TIn *)a.v_win + off;
-    len = a.win_len[w];
-  } else {
-    const int c = j - n_pool - sc;
-    const size_t off = (bh * a.Nq + (size_t)c * BT) * D;
-    kp = (const TIn *)a.k_cur + off;
-    vp = (const TIn *)a.v_cur + off;
-    len = min(BT, a.Nq - c * BT);
-  }
-  if (len < 0 || len > BT) {
-    set_status(a.status, PBSA_STATUS_WIN_LEN);
-    len = max(0, min(len, BT));
-  }
-}
-
 __device__ __forceinline__ void item_of_block(const FwdArgs &a, int &item) {
   const int n = blockIdx.x;
   item = (n & 7) * a.per_xcd + (n >> 3);
-}
-
-__device__ __forceinline__ int clamp_counts(const FwdArgs &a, size_t bh, int i, int &n_pool,
-                                            int &sc) {
-  n_pool = a.pool_count[bh];
-  if (n_pool < 0 || n_pool > a.C) {
-    set_status(a.status, PBSA_STATUS_POOL_COUNT);
-    n_pool = max(0, min(n_pool, a.C));
-  }
-  sc = a.sel_count[bh * a.QB + i];
-  if (sc < 0 || sc > a.topk) {
-    set_status(a.status, PBSA_STATUS_SEL);
-    sc = max(0, min(sc, a.topk));
-  }
-  return n_pool + sc + a.QB;
-}
-
-// The pool and selected-window part of a query block's list, resolved once
-// per workgroup into LDS: element offset of the block in its region and
-// (len | window << 16).  Entries past kMaxList fall back to resolve_block.
-constexpr int kMaxList = 128;
-
-struct BlockList {
-  int64_t off[kMaxList];
-  int32_t meta[kMaxList];
-};
-
-template <int D, int BT>
-__device__ __forceinline__ void preload_list(const FwdArgs &a, size_t bh, int i, int n_pool, int sc,
-                                             BlockList &bl, int t) {
-  const int n = min(n_pool + sc, kMaxList);
-  for (int j = t; j < n; j += 2 * BT) {
-    int64_t off;
-    int len, win = 0;
-    if (j < n_pool) {
-      off = (int64_t)(bh * a.C + j) * (BT * D);
-      len = a.pool_len[bh * a.C + j];
-    } else {
-      const int w = a.sel[(bh * a.QB + i) * (size_t)a.topk + (j - n_pool)];
-      win = 1;
-      if (w < 0 || w >= a.W) {
-        set_status(a.status, PBSA_STATUS_SEL);
-        off = 0;
-        len = 0;
-      } else {
-        off = (int64_t)(bh * a.W + w) * (BT * D);
-        len = a.win_len[w];
-      }
-    }
-    if (len < 0 || len > BT) {
-      set_status(a.status, PBSA_STATUS_WIN_LEN);
-      len = max(0, min(len, BT));
-    }
-    bl.off[j] = off;
-    bl.meta[j] = len | (win << 16);
-  }
-}
-
-template <int D, int BT>
-__device__ __forceinline__ void list_block(const FwdArgs &a, const BlockList &bl, size_t bh, int i,
-                                           int n_pool, int sc, int j, const uint16_t *&kp,
-                                           const uint16_t *&vp, int &len) {
-  if (j < n_pool + sc && j < kMaxList) {
-    const int64_t off = __builtin_amdgcn_readfirstlane((int)(bl.off[j] & 0xffffffff)) |
-                        ((int64_t)__builtin_amdgcn_readfirstlane((int)(bl.off[j] >> 32)) << 32);
-    const int meta = __builtin_amdgcn_readfirstlane(bl.meta[j]);
-    len = meta & 0xffff;
-    if (meta >> 16) {
-      kp = (const uint16_t *)a.k_win + off;
-      vp = (const uint16_t *)a.v_win + off;
-    } else {
-      kp = (const uint16_t *)a.k_pool + off;
-      vp = (const uint16_t *)a.v_pool + off;
-    }
-  } else {
-    resolve_block<uint16_t, D, BT>(a, bh, i, n_pool, sc, j, kp, vp, len);
-  }
 }
 
 // K/V move through LDS in tiles of 64 tokens (a 128-token block is two
@@ -233,7 +118,7 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kerne
   uint32_t kdma[G::NVAR], vdma[G::NVAR];
   dma_lane_offsets<D, TT, NW, kSwzK>(lane, kdma);
   dma_lane_offsets<D, TT, NW, kSwzV>(lane, vdma);
-  preload_list<D, BT>(a, bh, i, n_pool, sc, blist, t);
+  preload_list<D, BT>(a, bh, i, n_pool, sc, blist, t, 2 * BT);
   __syncthreads();
 
   // tile stream: (block j, half h); tile rows = min(64, len_j - 64 h)
