@@ -128,7 +128,7 @@ size_t pbsa_workspace_size(const pbsa_problem *p, int op) {
   if (!p || check_problem(p, op) != PBSA_OK) return 0;
   switch (op) {
     case PBSA_OP_SELECT: return pbsa::select_ws_bytes(*p);
-    case PBSA_OP_FWD: return 0;
+    case PBSA_OP_FWD: return pbsa::fwd_ws_bytes(*p);
     case PBSA_OP_BWD: return pbsa::bwd_ws_bytes(*p);
     case PBSA_OP_UPDATE: return pbsa::update_ws_bytes(*p);
     default: return 0;
@@ -157,8 +157,6 @@ int pbsa_select(const pbsa_problem *p, const void *q, const pbsa_kv *kv, int32_t
 int pbsa_attn_fwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const int32_t *sel,
                   const int32_t *sel_count, void *o, float *lse, void *ws, size_t ws_bytes,
                   pbsa_stream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   int rc = check_problem(p, PBSA_OP_FWD);
   if (rc) return rc;
   REQ(q);
@@ -167,8 +165,9 @@ int pbsa_attn_fwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const
   REQ(sel_count);
   REQ(o);
   if (lse && !aligned16(lse)) return fail(PBSA_ERR_ALIGN, "lse is not 16-byte aligned");
-  return hip_status(pbsa::launch_attn_fwd(*p, eff_scale(p), q, *kv, sel, sel_count, o, lse,
-                                          (hipStream_t)stream));
+  if (ws != nullptr && !aligned16(ws)) return fail(PBSA_ERR_ALIGN, "ws is not 16-byte aligned");
+  return hip_status(pbsa::launch_attn_fwd(*p, eff_scale(p), q, *kv, sel, sel_count, o, lse, ws,
+                                          ws_bytes, (hipStream_t)stream));
 }
 
 int pbsa_attn_bwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const int32_t *sel,

@@ -33,6 +33,8 @@
 #include "pbsa_internal.h"
 #include "pbsa_tiles.h"
 
+#include <atomic>
+
 namespace pbsa {
 
 struct FwdArgs {
@@ -43,6 +45,16 @@ struct FwdArgs {
   int32_t *status;
   int H, Nq, W, C, topk, QB, n_items, per_xcd;
   float sl2;  // scale * log2(e)
+  // balanced split (see split_range): NB list entries per item, G
+  // workgroups sharing U = n_items * NB block visits; partial results of
+  // items cut between workgroups go to part_o / part_ml and are merged by
+  // the last workgroup to finish its piece (cnt: arrival counters tagged
+  // with this launch's epoch).
+  int split, NB, G;
+  uint32_t epoch;
+  int64_t U;
+  float *part_o, *part_ml;
+  unsigned long long *cnt;
 };
 
 __device__ __forceinline__ void item_of_block(const FwdArgs &a, int &item) {
@@ -58,18 +70,50 @@ __device__ __forceinline__ void item_of_block(const FwdArgs &a, int &item) {
 // workgroups per CU.
 constexpr int kTile = 64;
 
+// Workgroup wg of a split launch covers block visits [u0, u1) of the
+// sequence item 0 entries 0..NB-1, item 1 entries 0..NB-1, ...; the
+// workgroup owning visit u is ((u + 1) G - 1) / U.
+__device__ __forceinline__ int64_t split_start(const FwdArgs &a, int wg) {
+  return (int64_t)wg * a.U / a.G;
+}
+__device__ __forceinline__ int split_owner(const FwdArgs &a, int64_t u) {
+  return (int)(((u + 1) * a.G - 1) / a.U);
+}
+
+// Arrival on an epoch-tagged counter (high word: launch epoch, low word:
+// arrivals in that launch); returns the arrivals including this one.
+__device__ __forceinline__ int arrive(unsigned long long *c, uint32_t epoch) {
+  unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while (true) {
+    const unsigned long long nv =
+        (uint32_t)(old >> 32) == epoch ? old + 1 : (((unsigned long long)epoch << 32) | 1ull);
+    const unsigned long long prev = atomicCAS(c, old, nv);
+    if (prev == old) return (int)(uint32_t)nv;
+    old = prev;
+  }
+}
+
 template <int D, int BT>
-__global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kernel(FwdArgs a) {
+struct FwdLds {
+  uint16_t Kb[2][kTile * D] __attribute__((aligned(1024)));
+  uint16_t Vb[2][kTile * D] __attribute__((aligned(1024)));
+  BlockList blist;
+  int last;
+};
+
+// Entries [j0, j1) of item `item`'s block list.  A whole item (0, NB)
+// writes O and LSE; a piece writes its unnormalised O^T, running max and row
+// sum to its partial slot, and the last piece to arrive merges all pieces of
+// the item in workgroup order (so the result does not depend on timing).
+template <int D, int BT>
+__device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh, int wg, int item,
+                                            int j0, int j1) {
   constexpr int NW = BT / 32;  // waves; wave w owns query rows [32w, 32w+32)
   constexpr int TT = kTile;
   using G = DmaGeom<D, TT, NW>;
-  __shared__ __attribute__((aligned(1024))) uint16_t Kb[2][TT * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vb[2][TT * D];
-  __shared__ BlockList blist;
-
-  int item;
-  item_of_block(a, item);
-  if (item >= a.n_items) return;
+  uint16_t (&Kb)[2][TT * D] = sh.Kb;
+  uint16_t (&Vb)[2][TT * D] = sh.Vb;
+  BlockList &blist = sh.blist;
   const int i = item % a.QB;
   const size_t bh = item / a.QB;
   const int t = threadIdx.x;
@@ -78,6 +122,7 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kerne
   const int l32 = lane & 31, g = lane >> 5;
   int n_pool, sc;
   const int nb = clamp_counts(a, bh, i, n_pool, sc);
+  const int jend = min(j1, nb);
 
   // this lane's query column, held as MFMA B fragments for the whole kernel
   const int qrow = i * BT + wave * 32 + l32;
@@ -118,20 +163,23 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kerne
   uint32_t kdma[G::NVAR], vdma[G::NVAR];
   dma_lane_offsets<D, TT, NW, kSwzK>(lane, kdma);
   dma_lane_offsets<D, TT, NW, kSwzV>(lane, vdma);
+  __syncthreads();  // the previous segment of this workgroup is done with LDS
   preload_list<D, BT>(a, bh, i, n_pool, sc, blist, t, 2 * BT);
   __syncthreads();
 
   // tile stream: (block j, half h); tile rows = min(64, len_j - 64 h)
-  int j = 0, h = 0;
+  int j = j0, h = 0;
   const uint16_t *kb, *vb;
-  int blen;
-  list_block<D, BT>(a, blist, bh, i, n_pool, sc, 0, kb, vb, blen);
-  int tlen = min(TT, blen);
-  dma_block<D, TT, NW, kSwzK>(Kb[0], kb, tlen, wave, lane, kdma);
-  dma_block<D, TT, NW, kSwzV>(Vb[0], vb, tlen, wave, lane, vdma);
+  int blen = 0, tlen = 0;
+  if (j0 < jend) {
+    list_block<D, BT>(a, blist, bh, i, n_pool, sc, j0, kb, vb, blen);
+    tlen = min(TT, blen);
+    dma_block<D, TT, NW, kSwzK>(Kb[0], kb, tlen, wave, lane, kdma);
+    dma_block<D, TT, NW, kSwzV>(Vb[0], vb, tlen, wave, lane, vdma);
+  }
   int buf = 0;
 
-  while (true) {
+  while (j0 < jend) {
     PBSA_WAIT_VM(0);  // this tile has landed (own loads) ...
     __syncthreads();  // ... for every wave, and every wave is done with the other buffer
     // next tile
@@ -141,9 +189,9 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kerne
     if (hn * TT >= blen || hn * TT >= BT) {
       jn = j + 1;
       hn = 0;
-      if (jn < nb) list_block<D, BT>(a, blist, bh, i, n_pool, sc, jn, kn, vn, bn);
+      if (jn < jend) list_block<D, BT>(a, blist, bh, i, n_pool, sc, jn, kn, vn, bn);
     }
-    const bool more = jn < nb;
+    const bool more = jn < jend;
     if (more) {
       nlen = min(TT, bn - hn * TT);
       dma_block<D, TT, NW, kSwzK>(Kb[buf ^ 1], kn + hn * TT * D, nlen, wave, lane, kdma);
@@ -244,8 +292,61 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kerne
     buf ^= 1;
   }
 
-  // epilogue: O = O^T / l, LSE = ln(sum exp(scale s))
   l += __shfl_xor(l, 32);
+  if (j0 > 0 || j1 < a.NB) {
+    // piece of a split item: publish it, and merge if it is the last one
+    const int64_t first_u = (int64_t)item * a.NB;
+    const int slot = 2 * wg + (split_start(a, wg) / a.NB == item ? 0 : 1);
+    {
+      float *po = a.part_o + ((size_t)slot * (2 * BT) + t) * (D / 2);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+          *reinterpret_cast<f32x4 *>(po + dt * 16 + 4 * e4) =
+              f32x4{oacc[dt][4 * e4], oacc[dt][4 * e4 + 1], oacc[dt][4 * e4 + 2], oacc[dt][4 * e4 + 3]};
+      float *pm = a.part_ml + ((size_t)slot * (2 * BT) + t) * 2;
+      pm[0] = m;
+      pm[1] = l;
+    }
+    __threadfence();
+    __syncthreads();
+    const int ga = split_owner(a, first_u), gb = split_owner(a, first_u + a.NB - 1);
+    if (t == 0) sh.last = arrive(a.cnt + item, a.epoch) == gb - ga + 1;
+    __syncthreads();
+    if (!sh.last) return;
+    __threadfence();
+    float M = -INFINITY, L = 0.f;
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
+    for (int gg = ga; gg <= gb; ++gg) {
+      const int sl = 2 * gg + (split_start(a, gg) / a.NB == item ? 0 : 1);
+      const float *po = a.part_o + ((size_t)sl * (2 * BT) + t) * (D / 2);
+      const float *pm = a.part_ml + ((size_t)sl * (2 * BT) + t) * 2;
+      const float mg = pm[0], lg = pm[1];
+      if (mg == -INFINITY) continue;
+      const float mn = fmaxf(M, mg);
+      const float ca = __builtin_amdgcn_exp2f(M - mn), cb = __builtin_amdgcn_exp2f(mg - mn);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const f32x4 v = *reinterpret_cast<const f32x4 *>(po + dt * 16 + 4 * e4);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc[dt][4 * e4 + k] = acc[dt][4 * e4 + k] * ca + v[k] * cb;
+        }
+      L = L * ca + lg * cb;
+      M = mn;
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = acc[dt];
+    m = M;
+    l = L;
+  }
+  // O = O^T / l, LSE = ln(sum exp(scale s))
   const float inv = 1.f / l;
   if (qrow < a.Nq) {
     uint16_t *op = (uint16_t *)a.o + (bh * a.Nq + qrow) * (size_t)D;
@@ -259,6 +360,25 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kerne
         *reinterpret_cast<u32x2 *>(op + dt * 32 + 8 * jj + 4 * g) = pk;
       }
     if (g == 0 && a.lse) a.lse[bh * a.Nq + qrow] = (m + __log2f(l)) * kLn2;
+  }
+}
+
+template <int D, int BT>
+__global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kernel(FwdArgs a) {
+  __shared__ FwdLds<D, BT> sh;
+  int wg;
+  item_of_block(a, wg);
+  if (!a.split) {
+    if (wg < a.n_items) fwd_segment<D, BT>(a, sh, wg, wg, 0, a.NB);
+    return;
+  }
+  if (wg >= a.G) return;
+  const int64_t u0 = split_start(a, wg), u1 = split_start(a, wg + 1);
+  for (int item = (int)(u0 / a.NB); (int64_t)item * a.NB < u1; ++item) {
+    const int64_t base = (int64_t)item * a.NB;
+    const int j0 = (int)(u0 > base ? u0 - base : 0);
+    const int j1 = (int)(u1 - base < a.NB ? u1 - base : a.NB);
+    fwd_segment<D, BT>(a, sh, wg, item, j0, j1);
   }
 }
 
@@ -344,9 +464,41 @@ __global__ __launch_bounds__(2 * BT) void attn_fwd_f32_kernel(FwdArgs a) {
   }
 }
 
+// Resident workgroups of the split launch: two per CU (LDS and VGPR
+// budget of the bf16 kernel), at most kSplitSlots.
+constexpr int kSplitSlots = 512;
+
+static int split_slots() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kSplitSlots;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = kSplitSlots / 2;
+    cached[dev] = 2 * n < kSplitSlots ? 2 * n : kSplitSlots;
+  }
+  return cached[dev];
+}
+
+static size_t split_part_o_bytes(const pbsa_problem &p) {
+  return align256((size_t)2 * kSplitSlots * (2 * p.T) * (p.d / 2) * sizeof(float));
+}
+static size_t split_part_ml_bytes(const pbsa_problem &p) {
+  return align256((size_t)2 * kSplitSlots * (2 * p.T) * 2 * sizeof(float));
+}
+
+size_t fwd_ws_bytes(const pbsa_problem &p) {
+  if (p.dtype != PBSA_BF16) return 0;
+  const size_t n_items = (size_t)p.B * p.H * ((p.Nq + p.T - 1) / p.T);
+  return split_part_o_bytes(p) + split_part_ml_bytes(p) +
+         align256(n_items * sizeof(unsigned long long));
+}
+
 hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
                            const int32_t *sel, const int32_t *sel_count, void *o, float *lse,
-                           hipStream_t st) {
+                           void *ws, size_t ws_bytes, hipStream_t st) {
+  static std::atomic<uint32_t> epoch_counter{0};
   FwdArgs a;
   a.q = q;
   a.k_cur = kv.k_cur; a.v_cur = kv.v_cur; a.k_win = kv.k_win; a.v_win = kv.v_win;
@@ -356,8 +508,33 @@ hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, co
   a.H = p.H; a.Nq = p.Nq; a.W = p.W; a.C = p.C; a.topk = p.topk;
   a.QB = (p.Nq + p.T - 1) / p.T;
   a.n_items = p.B * p.H * a.QB;
-  a.per_xcd = (a.n_items + 7) / 8;
+  a.NB = p.C + p.topk + a.QB;
   a.sl2 = scale * kLog2e;
+  a.U = (int64_t)a.n_items * a.NB;
+  a.split = 0;
+  a.G = 0;
+  a.epoch = 0;
+  a.part_o = a.part_ml = nullptr;
+  a.cnt = nullptr;
+  int n_wg = a.n_items;
+  const int64_t slots = split_slots();
+  // The split pays off only when one workgroup per query block would leave
+  // most resident slots idle: pieces that start mid-list lose the lockstep
+  // walk through the shared pool and current blocks that keeps them in L2.
+  if (p.dtype == PBSA_BF16 && ws != nullptr && ws_bytes >= fwd_ws_bytes(p) &&
+      2 * (int64_t)a.n_items <= slots) {
+    a.split = 1;
+    a.G = (int)(a.U < slots ? a.U : slots);
+    uint32_t e = ++epoch_counter;
+    if (e == 0) e = ++epoch_counter;
+    a.epoch = e;
+    char *w = reinterpret_cast<char *>(ws);
+    a.part_o = reinterpret_cast<float *>(w);
+    a.part_ml = reinterpret_cast<float *>(w + split_part_o_bytes(p));
+    a.cnt = reinterpret_cast<unsigned long long *>(w + split_part_o_bytes(p) + split_part_ml_bytes(p));
+    n_wg = a.G;
+  }
+  a.per_xcd = (n_wg + 7) / 8;
   const dim3 grid(8 * a.per_xcd);
   const dim3 block(2 * p.T);
 #define PBSA_FWD_CASE(DT, D_, T_, KERN)                         \

@@ -14,6 +14,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 size_t select_ws_bytes(const pbsa_problem &p);
 size_t select_lds_bytes(const pbsa_problem &p);
 size_t update_ws_bytes(const pbsa_problem &p);
+size_t fwd_ws_bytes(const pbsa_problem &p);
 size_t bwd_ws_bytes(const pbsa_problem &p);
 
 hipError_t launch_select(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
@@ -26,7 +27,7 @@ hipError_t launch_window_append(const pbsa_problem &p, const pbsa_kv &kv, void *
                                 int first_slot, int64_t first_id, hipStream_t st);
 hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
                            const int32_t *sel, const int32_t *sel_count, void *o, float *lse,
-                           hipStream_t st);
+                           void *ws, size_t ws_bytes, hipStream_t st);
 hipError_t launch_attn_bwd(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
                            const int32_t *sel, const int32_t *sel_count, const void *o,
                            const float *lse, const void *dout, void *dq, const pbsa_kv_grad &g,

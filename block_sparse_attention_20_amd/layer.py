@@ -20,7 +20,7 @@ class PBSALayer:
     key caches, routing outputs and attention outputs."""
 
     def __init__(self, B, H, d, T, Nq, W, C, topk, dtype=torch.bfloat16, scale=0.0,
-                 device="cuda", with_status=True):
+                 device="cuda", with_status=True, ws_fwd="own"):
         self.B, self.H, self.d, self.T, self.Nq, self.W, self.C, self.topk = B, H, d, T, Nq, W, C, topk
         self.dtype, self.device = dtype, device
         self.QB = (Nq + T - 1) // T
@@ -53,6 +53,10 @@ class PBSALayer:
         self.ws_select = P.workspace(self.prob, P.PBSA_OP_SELECT, device)
         self.ws_update = P.workspace(self.prob, P.PBSA_OP_UPDATE, device)
         self.ws_bwd = P.workspace(self.prob, P.PBSA_OP_BWD, device)
+        # forward workspace: "own" allocates one (balanced split launch), None
+        # runs one workgroup per query block, a tensor is shared (layers that
+        # run one after another on one stream can share it)
+        self.ws_fwd = P.workspace(self.prob, P.PBSA_OP_FWD, device) if isinstance(ws_fwd, str) else ws_fwd
         self._kv = None
 
     # -- state ---------------------------------------------------------------
@@ -91,7 +95,7 @@ class PBSALayer:
     def fwd(self, with_lse=True):
         t = self.t
         P.pbsa_attn_fwd(self.prob, t["q"], self.kv, t["sel"] if self.topk > 0 else None,
-                        t["sel_count"], t["o"], t["lse"] if with_lse else None)
+                        t["sel_count"], t["o"], t["lse"] if with_lse else None, self.ws_fwd)
 
     def bwd(self, dout: torch.Tensor, grads: Optional[dict] = None) -> dict:
         t = self.t

@@ -134,9 +134,11 @@ def pbsa_select(prob, q, kv: KV, sel, sel_count, mass_pool, mass_win, ws, stream
                              0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def pbsa_attn_fwd(prob, q, kv: KV, sel, sel_count, o, lse, stream=None):
+def pbsa_attn_fwd(prob, q, kv: KV, sel, sel_count, o, lse, ws=None, stream=None):
     _check(lib().pbsa_attn_fwd(ctypes.byref(prob), _p(q), ctypes.byref(kv), _p(sel), _p(sel_count),
-                               _p(o), _p(lse), None, 0, _stream(stream)))
+                               _p(o), _p(lse), _p(ws),
+                               0 if ws is None else ws.numel() * ws.element_size(),
+                               _stream(stream)))
 
 
 def pbsa_attn_bwd(prob, q, kv: KV, sel, sel_count, o, lse, dout, dq, grad: KVGrad, ws,

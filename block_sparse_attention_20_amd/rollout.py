@@ -45,9 +45,12 @@ class Rollout:
         self.window_chunks = window_chunks
         self.W = window_chunks * self.QB
         self.n_sink = n_sink
-        self.layers: List[PBSALayer] = [
-            PBSALayer(B, H, d, T, Nq, self.W, C, topk, dtype=dtype, scale=scale, device=device)
-            for _ in range(n_layers)]
+        first = PBSALayer(B, H, d, T, Nq, self.W, C, topk, dtype=dtype, scale=scale, device=device)
+        # the forwards of all layers run on one stream: one split workspace
+        self.layers: List[PBSALayer] = [first] + [
+            PBSALayer(B, H, d, T, Nq, self.W, C, topk, dtype=dtype, scale=scale, device=device,
+                      ws_fwd=first.ws_fwd)
+            for _ in range(n_layers - 1)]
         self.leaving = [torch.arange(p * self.QB, (p + 1) * self.QB, dtype=torch.int32, device=device)
                         for p in range(window_chunks)]
         self.t = 0

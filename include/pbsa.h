@@ -145,7 +145,14 @@ int pbsa_select(const pbsa_problem *p, const void *q, const pbsa_kv *kv, int32_t
  * of the window slots sel[i][0:sel_count[i]], and of the whole current chunk:
  *   O_r = softmax_u(scale * <Q_r, K_u>) V_u,   lse_r = log sum_u exp(scale <Q_r,K_u>)
  * (natural log).  o: [B,H,Nq,d] in the problem dtype; lse may be NULL.
- * Workspace: none required (ws may be NULL).
+ * Workspace: optional.  With ws == NULL (or ws_bytes below
+ * pbsa_workspace_size(p, PBSA_OP_FWD)) each query block runs in one
+ * workgroup.  With a large enough 16-byte-aligned ws (bf16 only) the
+ * query-block x list-entry visits are split evenly over the GPU's resident
+ * workgroups; a query block cut between workgroups is merged by the last
+ * piece to finish, in a fixed order, so results stay bitwise reproducible.
+ * ws needs no initialisation; calls that share one ws must not overlap
+ * in time (one stream is fine).
  */
 int pbsa_attn_fwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const int32_t *sel,
                   const int32_t *sel_count, void *o, float *lse, void *ws, size_t ws_bytes,

@@ -64,7 +64,12 @@ def test_validate_select_size_limit():
 
 def test_workspace_sizes():
     p = wan()
-    assert P.pbsa_workspace_size(p, P.PBSA_OP_FWD) == 0
+    # forward: optional split workspace - partial O^T (fp32) and (max, sum)
+    # for two pieces per resident workgroup, plus one counter per query block
+    ws_fwd = P.pbsa_workspace_size(p, P.PBSA_OP_FWD)
+    assert ws_fwd >= 2 * 512 * 256 * 64 * 4 + 2 * 512 * 256 * 2 * 4 + 12 * 37 * 8
+    f32 = wan(); f32.dtype = P.PBSA_F32
+    assert P.pbsa_workspace_size(f32, P.PBSA_OP_FWD) == 0
     ws_sel = P.pbsa_workspace_size(p, P.PBSA_OP_SELECT)
     # qbar [12,37,128] f32 + per-row softmax [12,37,106] f32, 256-byte aligned
     assert ws_sel >= 12 * 37 * 128 * 4 + 12 * 37 * 106 * 4

@@ -149,6 +149,33 @@ def test_select_and_fwd_match_oracle(name):
     assert L.status_bits() == 0
 
 
+@pytest.mark.parametrize("name", ["bf16_d128_T128_small", "bf16_d64_T64_multi", "bf16_d128_T64",
+                                  "empty_pool_and_window"])
+def test_fwd_split_and_one_block_per_workgroup_agree(name):
+    """The forward with a split workspace (query blocks cut between
+    workgroups, merged by the last piece) and without one (one workgroup per
+    query block) both match the oracle; on these small problems the split
+    runs one list entry per workgroup, so every query block is merged from
+    one piece per entry."""
+    shape, kw = CASES[name]
+    _log(f"case {name}")
+    st = syn.make_state(shape, 23, pad_value=float("nan"), **kw)
+    L = run(shape, st)
+    assert L.ws_fwd is not None
+    o_split = L.t["o"].float().cpu().numpy(); lse_split = L.t["lse"].cpu().numpy()
+    L.ws_fwd, ws = None, L.ws_fwd
+    L.fwd()
+    torch.cuda.synchronize()
+    L.ws_fwd = ws
+    o_one = L.t["o"].float().cpu().numpy(); lse_one = L.t["lse"].cpu().numpy()
+    gsel = L.t["sel"].cpu().numpy(); gcnt = L.t["sel_count"].cpu().numpy()
+    f = po.attn_fwd(st, gsel, gcnt, eff_scale(shape, 0.0), shape.T)
+    for o, lse, what in ((o_split, lse_split, "split"), (o_one, lse_one, "one per workgroup")):
+        check_close_bf16(o, f["o"], f"{name} {what}")
+        assert np.abs(lse - f["lse"]).max() <= 2e-3, what
+    assert L.status_bits() == 0
+
+
 def test_fwd_deterministic_and_fully_written():
     shape, kw = CASES["bf16_d64_T64_multi"]
     st = syn.make_state(shape, 3, **kw)
