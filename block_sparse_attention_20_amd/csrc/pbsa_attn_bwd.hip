@@ -11,7 +11,7 @@
 // D_r = <dO_r, O_r> and dS = P (dO V^T - D):
 //   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
 // Four launches:
-//   1. per query row: L = log2(e) lse and D, into arrays padded to whole
+//   1. per query row: L = log2(e) lse and -D, into arrays padded to whole
 //      query blocks (padding rows hold zeros);
 //   2. inverse selection lists: for every window slot, the query blocks that
 //      selected it (CSR, ascending query block, built per (b, h) from the
@@ -44,7 +44,7 @@ struct BwdArgs {
   const int32_t *win_len, *pool_len, *pool_count, *sel, *sel_count;
   const float *lse;
   uint16_t *dq, *dk_cur, *dv_cur, *dk_win, *dv_win, *dk_pool, *dv_pool;
-  float *Lp, *Dp;  // [bh][QB*T]: log2(e) lse and D per query row, zero padded
+  float *Lp, *Dp;  // [bh][QB*T]: log2(e) lse and -D per query row, zero padded
   int32_t *qptr, *qidx;
   int32_t *status;
   int H, Nq, W, C, topk, QB, n_items, per_xcd;
@@ -59,7 +59,7 @@ __device__ __forceinline__ int bwd_item(const BwdArgs &a) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. L_r = log2(e) lse_r and D_r = <dO_r, O_r>.  grid (ceil(bh*QB*T / rows
+// 1. L_r = log2(e) lse_r and -D_r = -<dO_r, O_r>.  grid (ceil(bh*QB*T / rows
 //    per block)), 256 threads; rows past Nq of each (b, h) get zeros.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const uint16_t *__restric
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (rp < rows_p && c == 0) {
-    Dp[rp] = acc;
+    Dp[rp] = -acc;
     Lp[rp] = ok ? lse[src] * kLog2e : 0.f;
   }
 }
@@ -99,14 +99,20 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const uint16_t *__restric
 // ---------------------------------------------------------------------------
 constexpr int kCsrChunk = 8192;
 
-__device__ __forceinline__ void csr_stage(int32_t *sl, const int32_t *sb, const int32_t *cb,
-                                          int base, int m, int topk, int W, int t) {
-  for (int e = t; e < m; e += 256) {
-    const int idx = base + e;
-    const int i = idx / topk, s = idx - i * topk;
-    const int w = s < cb[i] ? sb[idx] : -1;
+// entries [base, base + m) into sl[0, m), padded with -1 to a multiple of 16
+__device__ __forceinline__ int csr_stage(int32_t *sl, const int32_t *sb, const int32_t *cb,
+                                         int base, int m, int topk, int W, int t) {
+  const int mp = (m + 15) & ~15;
+  for (int e = t; e < mp; e += 256) {
+    int w = -1;
+    if (e < m) {
+      const int idx = base + e;
+      const int i = idx / topk, s = idx - i * topk;
+      w = s < cb[i] ? sb[idx] : -1;
+    }
     sl[e] = w >= 0 && w < W ? w : -1;  // out-of-range slots select nothing
   }
+  return mp;
 }
 
 __global__ __launch_bounds__(256) void bwd_csr_kernel(const int32_t *__restrict__ sel,
@@ -114,7 +120,7 @@ __global__ __launch_bounds__(256) void bwd_csr_kernel(const int32_t *__restrict_
                                                       int32_t *__restrict__ qptr,
                                                       int32_t *__restrict__ qidx, int H, int W,
                                                       int QB, int topk) {
-  __shared__ int32_t sl[kCsrChunk];
+  __shared__ __attribute__((aligned(16))) int32_t sl[kCsrChunk];
   __shared__ int32_t start[1024 + 1];
   __shared__ int32_t wsum[4];
   const size_t bh = (size_t)blockIdx.y * H + blockIdx.x;
@@ -126,14 +132,24 @@ __global__ __launch_bounds__(256) void bwd_csr_kernel(const int32_t *__restrict_
   for (int base = 0; base < n; base += kCsrChunk) {
     const int m = min(kCsrChunk, n - base);
     __syncthreads();
-    csr_stage(sl, sb, cb, base, m, topk, W, t);
+    const int mp = csr_stage(sl, sb, cb, base, m, topk, W, t);
     __syncthreads();
-    for (int e = 0; e < m; ++e) {
-      const int w = sl[e];
-      c0 += w == t;
-      c1 += w == t + 256;
-      c2 += w == t + 512;
-      c3 += w == t + 768;
+    for (int e = 0; e < mp; e += 16) {
+      int4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const int4 *>(&sl[e + 4 * k]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int ws[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int w = ws[q];
+          c0 += w == t;
+          c1 += w == t + 256;
+          c2 += w == t + 512;
+          c3 += w == t + 768;
+        }
+      }
     }
   }
   // exclusive scan over slots: thread t sums slots 4t..4t+3
@@ -175,15 +191,27 @@ __global__ __launch_bounds__(256) void bwd_csr_kernel(const int32_t *__restrict_
   for (int base = 0; base < n; base += kCsrChunk) {
     const int m = min(kCsrChunk, n - base);
     __syncthreads();
-    csr_stage(sl, sb, cb, base, m, topk, W, t);
+    const int mp = csr_stage(sl, sb, cb, base, m, topk, W, t);
     __syncthreads();
-    for (int e = 0; e < m; ++e) {
-      const int w = sl[e];
-      if (w < 0 || (w & 255) != t) continue;  // w < W <= 1024 here
-      const int i = (base + e) / topk;
-      const int k = w >> 8;
-      const int pos = k == 0 ? p0++ : k == 1 ? p1++ : k == 2 ? p2++ : p3++;
-      qi[pos] = i;
+    if (t >= W) continue;  // owns no slot (W <= 1024, so t < W covers every owner)
+    for (int e = 0; e < mp; e += 16) {
+      int4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const int4 *>(&sl[e + 4 * k]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int ws[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int w = ws[q];
+          if (w >= 0 && (w & 255) == t) {  // w < W <= 1024 here
+            const int i = (base + e + 4 * k + q) / topk;
+            const int kk = w >> 8;
+            const int pos = kk == 0 ? p0++ : kk == 1 ? p1++ : kk == 2 ? p2++ : p3++;
+            qi[pos] = i;
+          }
+        }
+      }
     }
   }
 }
@@ -254,7 +282,7 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dq_kernel(BwdAr
   }
   const size_t prow = bh * (size_t)(a.QB * BT) + qrow;
   const float Lq = a.Lp[prow];
-  const float Dq = a.Dp[prow];
+  const float Dn = a.Dp[prow];  // -D of this query row
   const float sl2 = a.sl2;
   f32x16 dqacc[D / 32];
 #pragma unroll
@@ -323,13 +351,19 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dq_kernel(BwdAr
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc, 0, 0, 0);
           pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[kk], pacc, 0, 0, 0);
         }
-        // dS^T = P^T (dP^T - D); tokens past the tile's length are masked
-        const bool ragged = tlen < hf * 32 + 32;
+        // dS^T = P^T (dP^T - D); tokens past the tile's length (only in the
+        // ragged last tile of a block) get P = 0
+        if (tlen >= hf * 32 + 32) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float p = __builtin_amdgcn_exp2f(sacc[e] * sl2 - Lq);
-          if (ragged && hf * 32 + 8 * (e >> 2) + 4 * g + (e & 3) >= tlen) p = 0.f;
-          sacc[e] = p * (pacc[e] - Dq);
+          for (int e = 0; e < 16; ++e)
+            sacc[e] = __builtin_amdgcn_exp2f(sacc[e] * sl2 - Lq) * (pacc[e] + Dn);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            float p = __builtin_amdgcn_exp2f(sacc[e] * sl2 - Lq);
+            if (hf * 32 + 8 * (e >> 2) + 4 * g + (e & 3) >= tlen) p = 0.f;
+            sacc[e] = p * (pacc[e] + Dn);
+          }
         }
         // dQ^T += K^T dS^T, 16 tokens per step
 #pragma unroll
@@ -495,9 +529,18 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dkv_kernel(BwdA
         if (qs * 32 < tlen) {
           // S = Q K^T and dP = dO V^T over 32 query rows (element e of a
           // lane is query row 32 qs + 8 (e / 4) + 4 g + e % 4)
+          // dP accumulates onto -D, so it ends as dP - D (element e of a
+          // lane and float e % 4 of the LD read 4 (e / 4) share their row)
           f32x16 sacc, pacc;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) sacc[e] = pacc[e] = 0.f;
+          for (int m4 = 0; m4 < 4; ++m4) {
+            const f32x4 D4 = *reinterpret_cast<const f32x4 *>(&Dl[qs * 32 + 8 * m4 + 4 * g]);
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+              sacc[4 * m4 + e4] = 0.f;
+              pacc[4 * m4 + e4] = D4[e4];
+            }
+          }
 #pragma unroll
           for (int kk = 0; kk < D / 16; ++kk) {
             const int ro = qs * 32 * D + (rbase ^ (16 * kk));
@@ -511,13 +554,12 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dkv_kernel(BwdA
 #pragma unroll
           for (int m4 = 0; m4 < 4; ++m4) {
             const f32x4 L4 = *reinterpret_cast<const f32x4 *>(&Ll[qs * 32 + 8 * m4 + 4 * g]);
-            const f32x4 D4 = *reinterpret_cast<const f32x4 *>(&Dl[qs * 32 + 8 * m4 + 4 * g]);
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4) {
               const int e = 4 * m4 + e4;
               const float p = __builtin_amdgcn_exp2f(sacc[e] * sl2 - L4[e4]);
               sacc[e] = p;
-              pacc[e] = p * (pacc[e] - D4[e4]);
+              pacc[e] = p * pacc[e];
             }
           }
           // dV^T += dO^T P and dK^T += Q^T dS, 16 query rows per step
