@@ -115,6 +115,83 @@ __device__ __forceinline__ int csr_stage(int32_t *sl, const int32_t *sb, const i
   return mp;
 }
 
+// In place: start[0..W) holds per-slot counts (W <= 1024); afterwards
+// start[w] is the exclusive prefix sum and start[W] the total.  256 threads;
+// thread t sums slots 4t..4t+3, then a wave scan and a scan of wave totals.
+__device__ __forceinline__ void csr_exclusive_scan(int32_t *start, int32_t *wsum, int W, int t) {
+  const int lane = t & 63, wave = t >> 6;
+  __syncthreads();
+  int v[4], s = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[k] = 4 * t + k < W ? start[4 * t + k] : 0;
+    s += v[k];
+  }
+  int incl = s;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int run = incl - s;
+  for (int w2 = 0; w2 < wave; ++w2) run += wsum[w2];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    start[4 * t + k] = run;
+    run += v[k];
+  }
+  if (t == 255) start[1024] = run;
+  __syncthreads();
+  if (t == 0) start[W] = start[1024];
+  __syncthreads();
+}
+
+// Small problems (QB * W <= kCsrMat): per (query block, slot) selection
+// counts in LDS; each slot's list is then a scan over query blocks.
+constexpr int kCsrMat = 12288;
+
+__global__ __launch_bounds__(256) void bwd_csr_mat_kernel(const int32_t *__restrict__ sel,
+                                                          const int32_t *__restrict__ sel_count,
+                                                          int32_t *__restrict__ qptr,
+                                                          int32_t *__restrict__ qidx, int H, int W,
+                                                          int QB, int topk) {
+  __shared__ int32_t mat[kCsrMat];
+  __shared__ int32_t start[1024 + 1];
+  __shared__ int32_t wsum[4];
+  const size_t bh = (size_t)blockIdx.y * H + blockIdx.x;
+  const int t = threadIdx.x;
+  const int32_t *sb = sel + bh * QB * (size_t)topk;
+  const int32_t *cb = sel_count + bh * QB;
+  for (int e = t; e < QB * W; e += 256) mat[e] = 0;
+  __syncthreads();
+  for (int e = t; e < QB * topk; e += 256) {
+    const int i = e / topk, s = e - i * topk;
+    if (s < cb[i]) {
+      const int w = sb[e];
+      if (w >= 0 && w < W) atomicAdd(&mat[i * W + w], 1);  // out-of-range slots select nothing
+    }
+  }
+  __syncthreads();
+  for (int w = t; w < 1024; w += 256) {
+    int c = 0;
+    if (w < W)
+      for (int i = 0; i < QB; ++i) c += mat[i * W + w];
+    start[w] = c;
+  }
+  csr_exclusive_scan(start, wsum, W, t);
+  int32_t *qp = qptr + bh * (W + 1);
+  int32_t *qi = qidx + bh * QB * (size_t)topk;
+  for (int w = t; w <= W; w += 256) qp[w] = start[w];
+  for (int w = t; w < W; w += 256) {
+    int pos = start[w];
+    for (int i = 0; i < QB; ++i)
+      for (int c = mat[i * W + w]; c > 0; --c) qi[pos++] = i;
+  }
+}
+
 __global__ __launch_bounds__(256) void bwd_csr_kernel(const int32_t *__restrict__ sel,
                                                       const int32_t *__restrict__ sel_count,
                                                       int32_t *__restrict__ qptr,
@@ -124,7 +201,7 @@ __global__ __launch_bounds__(256) void bwd_csr_kernel(const int32_t *__restrict_
   __shared__ int32_t start[1024 + 1];
   __shared__ int32_t wsum[4];
   const size_t bh = (size_t)blockIdx.y * H + blockIdx.x;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x;
   const int32_t *sb = sel + bh * QB * (size_t)topk;
   const int32_t *cb = sel_count + bh * QB;
   const int n = QB * topk;
@@ -152,40 +229,14 @@ __global__ __launch_bounds__(256) void bwd_csr_kernel(const int32_t *__restrict_
       }
     }
   }
-  // exclusive scan over slots: thread t sums slots 4t..4t+3
   __syncthreads();
   start[t] = c0;
   start[t + 256] = c1;
   start[t + 512] = c2;
   start[t + 768] = c3;
-  __syncthreads();
-  int v[4], s = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    v[k] = 4 * t + k < W ? start[4 * t + k] : 0;
-    s += v[k];
-  }
-  int incl = s;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  int run = incl - s;
-  for (int w2 = 0; w2 < wave; ++w2) run += wsum[w2];
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    start[4 * t + k] = run;
-    run += v[k];
-  }
-  if (t == 255) start[1024] = run;
-  __syncthreads();
+  csr_exclusive_scan(start, wsum, W, t);
   int32_t *qp = qptr + bh * (W + 1);
-  for (int w = t; w < W; w += 256) qp[w] = start[w];
-  if (t == 0) qp[W] = start[W];
+  for (int w = t; w <= W; w += 256) qp[w] = start[w];
   int p0 = start[t], p1 = start[t + 256], p2 = start[t + 512], p3 = start[t + 768];
   int32_t *qi = qidx + bh * QB * (size_t)topk;
   for (int base = 0; base < n; base += kCsrChunk) {
@@ -667,8 +718,14 @@ hipError_t launch_attn_bwd(const pbsa_problem &p, float scale, const void *q, co
     bwd_rows_kernel<128><<<rblocks, 256, 0, st>>>(a.o, a.dout, lse, a.Lp, a.Dp, rows_p, p.Nq, NqP);
   else
     bwd_rows_kernel<64><<<rblocks, 256, 0, st>>>(a.o, a.dout, lse, a.Lp, a.Dp, rows_p, p.Nq, NqP);
-  if (p.W > 0 && p.topk > 0)
-    bwd_csr_kernel<<<dim3(p.H, p.B), 256, 0, st>>>(sel, sel_count, a.qptr, a.qidx, p.H, p.W, a.QB, p.topk);
+  if (p.W > 0 && p.topk > 0) {
+    if ((int64_t)a.QB * p.W <= kCsrMat)
+      bwd_csr_mat_kernel<<<dim3(p.H, p.B), 256, 0, st>>>(sel, sel_count, a.qptr, a.qidx, p.H, p.W,
+                                                         a.QB, p.topk);
+    else
+      bwd_csr_kernel<<<dim3(p.H, p.B), 256, 0, st>>>(sel, sel_count, a.qptr, a.qidx, p.H, p.W,
+                                                     a.QB, p.topk);
+  }
 
   const dim3 block(2 * p.T);
 #define PBSA_BWD_CASE(D_, T_)                                                     \

@@ -66,6 +66,10 @@ CASES = {
                  dict(sigma=1.0, n_planted=2, shift=1.0, pool_count=3)),
     "current_only": (syn.Shape(B=1, H=2, d=128, T=128, Nq=100, W=0, C=0, topk=0),
                      dict(sigma=1.0, win_len=[], pool_count=0)),
+    # 100 query blocks x 128 window slots: the inverse selection no longer fits
+    # the per-(query block, slot) count table and takes the streaming scan
+    "many_slots": (syn.Shape(B=1, H=1, d=64, T=64, Nq=100 * 64 - 10, W=128, C=2, topk=4),
+                   dict(sigma=1.0, shift=1.0, n_planted=4, pool_count=2)),
 }
 
 
