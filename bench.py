@@ -37,19 +37,31 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # --pmc passes (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by
 # what the same counter reads for a copy kernel of known size (the window
 # append: 28,302 KiB read and 28,302 KiB written per launch; it reads back
-# FETCH 14,166 KiB, WRITE 28,304 KiB).  Valid only for the kernel source it
-# was measured on (sha1 below); reported as null once that source changes.
-FWD_TRAFFIC = {"src_sha1": "373cc33055a158ee7e5156a3df8bfa3b37180dd6",
-               "fetch_kib": 59748.0, "write_kib": 14259.55,
-               "fetch_scale": 28302.0 / 14166.05, "write_scale": 28302.0 / 28304.32}
+# FETCH 14,167 KiB, WRITE 28,304 KiB).  Valid only for the kernel source it
+# was measured on (sha1 over FWD_SOURCES below); reported as null once those
+# sources change.
+FWD_TRAFFIC = {"src_sha1": "3ab3c4adb530afdcf74ddb651d091267d30f2c8e",
+               "fetch_kib": 61757.6, "write_kib": 14259.6,
+               "fetch_scale": 28302.0 / 14166.7, "write_scale": 28302.0 / 28304.3}
+
+
+FWD_SOURCES = ("pbsa_attn_fwd.hip", "pbsa_tiles.h")
+
+
+def fwd_source_sha1() -> str:
+    """sha1 over the forward kernel's sources (the kernel file and the tile
+    staging header it includes)."""
+    import hashlib
+    h = hashlib.sha1()
+    for name in FWD_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_attention_20_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def fwd_traffic_bytes():
-    import hashlib
-    src = os.path.join(ROOT, "block_sparse_attention_20_amd", "csrc", "pbsa_attn_fwd.hip")
-    with open(src, "rb") as f:
-        if hashlib.sha1(f.read()).hexdigest() != FWD_TRAFFIC["src_sha1"]:
-            return None
+    if fwd_source_sha1() != FWD_TRAFFIC["src_sha1"]:
+        return None
     t = FWD_TRAFFIC
     return round(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]))
 
