@@ -34,6 +34,8 @@
 #include "pbsa_tiles.h"
 
 #include <atomic>
+#include <chrono>
+#include <type_traits>
 
 namespace pbsa {
 
@@ -81,7 +83,9 @@ __device__ __forceinline__ int split_owner(const FwdArgs &a, int64_t u) {
 }
 
 // Arrival on an epoch-tagged counter (high word: launch epoch, low word:
-// arrivals in that launch); returns the arrivals including this one.
+// arrivals in that launch); returns the arrivals including this one.  A
+// word with another epoch (garbage, or an earlier launch) counts as zero, and
+// the last arrival of a launch resets it to zero.
 __device__ __forceinline__ int arrive(unsigned long long *c, uint32_t epoch) {
   unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   while (true) {
@@ -177,9 +181,10 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
     dma_block<D, TT, NW, kSwzK>(Kb[0], kb, tlen, wave, lane, kdma);
     dma_block<D, TT, NW, kSwzV>(Vb[0], vb, tlen, wave, lane, vdma);
   }
-  int buf = 0;
-
-  while (j0 < jend) {
+  // the two LDS buffers alternate; each is a compile-time index so that
+  // tile addresses are immediate offsets
+  auto step = [&](auto bufc) __attribute__((always_inline)) -> bool {
+    constexpr int buf = decltype(bufc)::value;
     PBSA_WAIT_VM(0);  // this tile has landed (own loads) ...
     __syncthreads();  // ... for every wave, and every wave is done with the other buffer
     // next tile
@@ -192,10 +197,20 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
       if (jn < jend) list_block<D, BT>(a, blist, bh, i, n_pool, sc, jn, kn, vn, bn);
     }
     const bool more = jn < jend;
+    // the next tile's DMA: a ragged tile is issued here; a full one is
+    // spread over the k-steps of S below, between the MFMAs
+    bool dfull = false;
+    const char *kd = nullptr, *vd = nullptr;
     if (more) {
       nlen = min(TT, bn - hn * TT);
-      dma_block<D, TT, NW, kSwzK>(Kb[buf ^ 1], kn + hn * TT * D, nlen, wave, lane, kdma);
-      dma_block<D, TT, NW, kSwzV>(Vb[buf ^ 1], vn + hn * TT * D, nlen, wave, lane, vdma);
+      if (nlen < TT) {
+        dma_block<D, TT, NW, kSwzK>(Kb[buf ^ 1], kn + hn * TT * D, nlen, wave, lane, kdma);
+        dma_block<D, TT, NW, kSwzV>(Vb[buf ^ 1], vn + hn * TT * D, nlen, wave, lane, vdma);
+      } else {
+        dfull = true;
+        kd = reinterpret_cast<const char *>(kn + hn * TT * D + (size_t)wave * G::IPW * G::RPI * D);
+        vd = reinterpret_cast<const char *>(vn + hn * TT * D + (size_t)wave * G::IPW * G::RPI * D);
+      }
     }
     const uint16_t *Kl = Kb[buf];
     const uint16_t *Vl = Vb[buf];
@@ -207,20 +222,43 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[tt][e] = 0.f;
     {
-      bf16x8 ka[2][TT / 32];  // K fragments, one k-step ahead of the MFMAs
+      constexpr int PD = 2;  // K fragments PD k-steps ahead of the MFMAs
+      bf16x8 ka[PD + 1][TT / 32];
 #pragma unroll
-      for (int tt = 0; tt < TT / 32; ++tt)
-        ka[0][tt] = *reinterpret_cast<const bf16x8 *>(&Kl[tt * 32 * D + koff[0]]);
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        if (kk + 1 < D / 16) {
-#pragma unroll
-          for (int tt = 0; tt < TT / 32; ++tt)
-            ka[(kk + 1) & 1][tt] = *reinterpret_cast<const bf16x8 *>(&Kl[tt * 32 * D + koff[kk + 1]]);
-        }
+      for (int k0 = 0; k0 < PD; ++k0)
 #pragma unroll
         for (int tt = 0; tt < TT / 32; ++tt)
-          sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk & 1][tt], qf[kk], sacc[tt], 0, 0, 0);
+          ka[k0][tt] = *reinterpret_cast<const bf16x8 *>(&Kl[tt * 32 * D + koff[k0]]);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        if (kk + PD < D / 16) {
+#pragma unroll
+          for (int tt = 0; tt < TT / 32; ++tt)
+            ka[(kk + PD) % (PD + 1)][tt] = *reinterpret_cast<const bf16x8 *>(&Kl[tt * 32 * D + koff[kk + PD]]);
+        }
+        // this k-step's share of the next tile's DMA (2 IPW instructions
+        // over D/16 steps)
+        if (dfull) {
+          constexpr int NI = 2 * G::IPW, PER = (NI + D / 16 - 1) / (D / 16);
+#pragma unroll
+          for (int q = 0; q < PER; ++q) {
+            const int it2 = kk * PER + q;
+            if (it2 < NI) {
+              const bool isv = it2 >= G::IPW;
+              const int it = isv ? it2 - G::IPW : it2;
+              const char *src = (isv ? vd : kd) + (it / G::NVAR) * (G::NVAR * G::RPI * D * 2) +
+                                (isv ? vdma : kdma)[it % G::NVAR];
+              uint16_t *dst = (isv ? Vb[buf ^ 1] : Kb[buf ^ 1]) + wave * G::IPW * 512 + it * 512;
+              __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
+            }
+          }
+        }
+#pragma unroll
+        for (int tt = 0; tt < TT / 32; ++tt) {
+          // an empty asm on the fragment keeps this MFMA after the reads above
+          asm volatile("" : "+v"(ka[kk % (PD + 1)][tt]));
+          sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % (PD + 1)][tt], qf[kk], sacc[tt], 0, 0, 0);
+        }
       }
     }
     // ---- online softmax (log2 domain); the running max only moves when a
@@ -282,15 +320,18 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st & 1][dt], pf, oacc[dt], 0, 0, 0);
       }
     }
-    if (!more) break;
+    if (!more) return false;
     j = jn;
     h = hn;
     kb = kn;
     vb = vn;
     blen = bn;
     tlen = nlen;
-    buf ^= 1;
-  }
+    return true;
+  };
+  if (j0 < jend)
+    while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
+    }
 
   l += __shfl_xor(l, 32);
   if (j0 > 0 || j1 < a.NB) {
@@ -312,7 +353,11 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
     __threadfence();
     __syncthreads();
     const int ga = split_owner(a, first_u), gb = split_owner(a, first_u + a.NB - 1);
-    if (t == 0) sh.last = arrive(a.cnt + item, a.epoch) == gb - ga + 1;
+    if (t == 0) {
+      sh.last = arrive(a.cnt + item, a.epoch) == gb - ga + 1;
+      // every piece of this launch has arrived: leave the counter at zero
+      if (sh.last) __hip_atomic_store(a.cnt + item, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
     if (!sh.last) return;
     __threadfence();
@@ -498,7 +543,11 @@ size_t fwd_ws_bytes(const pbsa_problem &p) {
 hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
                            const int32_t *sel, const int32_t *sel_count, void *o, float *lse,
                            void *ws, size_t ws_bytes, hipStream_t st) {
-  static std::atomic<uint32_t> epoch_counter{0};
+  // launch epochs: consecutive from a start that differs between library
+  // instances, so a workspace handed over from another instance in the same
+  // process cannot match
+  static std::atomic<uint32_t> epoch_counter{
+      (uint32_t)((uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761ull)};
   FwdArgs a;
   a.q = q;
   a.k_cur = kv.k_cur; a.v_cur = kv.v_cur; a.k_win = kv.k_win; a.v_win = kv.v_win;

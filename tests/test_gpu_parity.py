@@ -176,6 +176,23 @@ def test_fwd_split_and_one_block_per_workgroup_agree(name):
     assert L.status_bits() == 0
 
 
+def test_fwd_split_workspace_needs_no_initialisation():
+    """The split forward's workspace may hold anything (here: bytes of an
+    earlier use, then random bytes): arrival counters only count words
+    tagged with the running launch, so the result matches a clean run."""
+    shape, kw = CASES["bf16_d64_T64_multi"]
+    st = syn.make_state(shape, 31, **kw)
+    L = run(shape, st)
+    ref_o = L.t["o"].clone(); ref_l = L.t["lse"].clone()
+    g = torch.Generator(device="cuda").manual_seed(5)
+    for _ in range(2):
+        L.ws_fwd.copy_(torch.randint(0, 256, L.ws_fwd.shape, generator=g, device="cuda",
+                                     dtype=torch.int32).to(torch.uint8))
+        L.fwd()
+        torch.cuda.synchronize()
+        assert torch.equal(L.t["o"], ref_o) and torch.equal(L.t["lse"], ref_l)
+
+
 def test_fwd_deterministic_and_fully_written():
     shape, kw = CASES["bf16_d64_T64_multi"]
     st = syn.make_state(shape, 3, **kw)
