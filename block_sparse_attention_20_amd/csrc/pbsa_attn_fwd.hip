@@ -208,8 +208,8 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
         dma_block<D, TT, NW, kSwzV>(Vb[buf ^ 1], vn + hn * TT * D, nlen, wave, lane, vdma);
       } else {
         dfull = true;
-        kd = reinterpret_cast<const char *>(kn + hn * TT * D + (size_t)wave * G::IPW * G::RPI * D);
-        vd = reinterpret_cast<const char *>(vn + hn * TT * D + (size_t)wave * G::IPW * G::RPI * D);
+        kd = dma_wave_src<D, TT, NW>(kn + hn * TT * D, wave);
+        vd = dma_wave_src<D, TT, NW>(vn + hn * TT * D, wave);
       }
     }
     const uint16_t *Kl = Kb[buf];
@@ -243,14 +243,10 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
 #pragma unroll
           for (int q = 0; q < PER; ++q) {
             const int it2 = kk * PER + q;
-            if (it2 < NI) {
-              const bool isv = it2 >= G::IPW;
-              const int it = isv ? it2 - G::IPW : it2;
-              const char *src = (isv ? vd : kd) + (it / G::NVAR) * (G::NVAR * G::RPI * D * 2) +
-                                (isv ? vdma : kdma)[it % G::NVAR];
-              uint16_t *dst = (isv ? Vb[buf ^ 1] : Kb[buf ^ 1]) + wave * G::IPW * 512 + it * 512;
-              __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
-            }
+            if (it2 < G::IPW)
+              dma_one<D, TT, NW>(Kb[buf ^ 1], kd, wave, it2, kdma);
+            else if (it2 < NI)
+              dma_one<D, TT, NW>(Vb[buf ^ 1], vd, wave, it2 - G::IPW, vdma);
           }
         }
 #pragma unroll

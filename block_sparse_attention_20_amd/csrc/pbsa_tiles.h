@@ -98,6 +98,21 @@ __device__ __forceinline__ void dma_block(uint16_t *lds, const uint16_t *src, in
   }
 }
 
+// The same full-tile DMA one instruction at a time, so that a kernel can
+// spread a tile's loads between its MFMAs: `wsrc` is the block's first row
+// of this wave's share (src + wave * IPW * RPI rows), `it` < IPW.
+template <int D, int BT, int NW>
+__device__ __forceinline__ void dma_one(uint16_t *lds, const char *wsrc, int wave, int it,
+                                        const uint32_t *ofs) {
+  using G = DmaGeom<D, BT, NW>;
+  const char *g = wsrc + (it / G::NVAR) * (G::NVAR * G::RPI * D * 2) + ofs[it % G::NVAR];
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)(lds + wave * G::IPW * 512 + it * 512), 16, 0, 0);
+}
+template <int D, int BT, int NW>
+__device__ __forceinline__ const char *dma_wave_src(const uint16_t *src, int wave) {
+  using G = DmaGeom<D, BT, NW>;
+  return reinterpret_cast<const char *>(src + (size_t)wave * G::IPW * G::RPI * D);
+}
 
 // A = V^T / K^T / Q^T fragment of a 32x32x16 MFMA read from a row-major
 // [rows][D] tile with ds_read_b64_tr_b16: two 4-row bands (rows r1 and
