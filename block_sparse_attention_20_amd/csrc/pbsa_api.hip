@@ -68,7 +68,7 @@ int hip_status(hipError_t e) {
   return fail(PBSA_ERR_HIP, "HIP error %d: %s", (int)e, hipGetErrorString(e));
 }
 
-int check_ws(const pbsa_problem *p, int op, void *ws, size_t ws_bytes) {
+int check_ws(const pbsa_problem *p, int op, const void *ws, size_t ws_bytes) {
   const size_t need = pbsa_workspace_size(p, op);
   if (need == 0) return PBSA_OK;
   if (!ws) return fail(PBSA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
@@ -147,11 +147,23 @@ int pbsa_select(const pbsa_problem *p, const void *q, const pbsa_kv *kv, int32_t
   if (p->C > 0) REQ(kv->kbar_pool);
   if (p->topk > 0) REQ(sel);
   REQ(sel_count);
+  const bool masses = mass_pool != nullptr || mass_win != nullptr;
+  if (masses && p->C > 0) REQ(mass_pool);
+  if (masses && p->W > 0) REQ(mass_win);
+  if ((rc = check_ws(p, PBSA_OP_SELECT, ws, ws_bytes))) return rc;
+  return hip_status(pbsa::launch_select(*p, eff_scale(p), q, *kv, sel, sel_count,
+                                        masses ? mass_pool : nullptr, masses ? mass_win : nullptr,
+                                        masses, ws, (hipStream_t)stream));
+}
+
+int pbsa_block_mass(const pbsa_problem *p, float *mass_pool, float *mass_win, const void *ws,
+                    size_t ws_bytes, pbsa_stream_t stream) {
+  int rc = check_problem(p, PBSA_OP_SELECT);
+  if (rc) return rc;
   if (p->C > 0) REQ(mass_pool);
   if (p->W > 0) REQ(mass_win);
   if ((rc = check_ws(p, PBSA_OP_SELECT, ws, ws_bytes))) return rc;
-  return hip_status(pbsa::launch_select(*p, eff_scale(p), q, *kv, sel, sel_count, mass_pool,
-                                        mass_win, ws, (hipStream_t)stream));
+  return hip_status(pbsa::launch_block_mass(*p, mass_pool, mass_win, ws, (hipStream_t)stream));
 }
 
 int pbsa_attn_fwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const int32_t *sel,

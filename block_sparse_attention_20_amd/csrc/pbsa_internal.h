@@ -19,7 +19,9 @@ size_t bwd_ws_bytes(const pbsa_problem &p);
 
 hipError_t launch_select(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
                          int32_t *sel, int32_t *sel_count, float *mass_pool, float *mass_win,
-                         void *ws, hipStream_t st);
+                         bool masses, void *ws, hipStream_t st);
+hipError_t launch_block_mass(const pbsa_problem &p, float *mass_pool, float *mass_win,
+                             const void *ws, hipStream_t st);
 hipError_t launch_block_mean(const pbsa_problem &p, const void *x, const int32_t *len,
                              int64_t n_blocks, float *out, hipStream_t st);
 hipError_t launch_window_append(const pbsa_problem &p, const pbsa_kv &kv, void *k_win, void *v_win,

@@ -119,7 +119,9 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
   int64_t *wid = reinterpret_cast<int64_t *>(qv + 128);   // [W]
   float *s = reinterpret_cast<float *>(wid + W);          // [C + W]
   int *flag = reinterpret_cast<int *>(s + C + W);         // [W]: 1 valid, 2 selected
+  int *rank = flag + W;                                    // [W]
   __shared__ int nvalid_sh;
+  __shared__ int wcnt[4];
 
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t bh = (size_t)b * H + h;
@@ -192,26 +194,45 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
   }
   __syncthreads();
 
-  // rank-based top-k over the valid window slots
-  for (int w = t; w < W; w += 256) {
-    if (!(flag[w] & 1)) continue;
-    const float sw = s[C + w];
-    const int64_t iw = wid[w];
-    int rank = 0;
-#pragma unroll 8
-    for (int v = 0; v < W; ++v)
-      rank += (flag[v] & 1) && v != w && ranks_before(s[C + v], wid[v], sw, iw);
-    if (rank < topk) flag[w] |= 2;
+  // rank-based top-k over the valid window slots: a slot is selected iff
+  // fewer than k valid slots rank before it.  The comparisons are split
+  // over the four waves (each takes a quarter of the v range for every w);
+  // partial ranks meet in LDS.
+  for (int w = t; w < W; w += 256) rank[w] = 0;
+  __syncthreads();
+  {
+    const int vq = (W + 3) / 4, v0 = wave * vq, v1 = min(W, v0 + vq);
+    for (int w = lane; w < W; w += 64) {
+      if (!(flag[w] & 1)) continue;
+      const float sw = s[C + w];
+      const int64_t iw = wid[w];
+      int r = 0;
+#pragma unroll 4
+      for (int v = v0; v < v1; ++v)
+        r += (flag[v] & 1) && v != w && ranks_before(s[C + v], wid[v], sw, iw);
+      if (r) atomicAdd(&rank[w], r);
+    }
   }
+  __syncthreads();
+  for (int w = t; w < W; w += 256)
+    if ((flag[w] & 1) && rank[w] < topk) flag[w] |= 2;
   __syncthreads();
   const int n_sel = min(topk, nvalid_sh);
   int32_t *selrow = sel + (bh * QB + i) * (size_t)topk;
-  for (int w = t; w < W; w += 256) {
-    if (!(flag[w] & 2)) continue;
-    int pos = 0;
-#pragma unroll 8
-    for (int v = 0; v < w; ++v) pos += (flag[v] >> 1) & 1;
-    selrow[pos] = w;
+  // positions: ascending slot order, by ballot prefix counts per 256 slots
+  int carry = 0;
+  for (int base = 0; base < W; base += 256) {
+    const int w = base + t;
+    const bool bit = w < W && (flag[w] & 2);
+    const unsigned long long m = __ballot(bit);
+    if (lane == 0) wcnt[wave] = __popcll(m);
+    __syncthreads();
+    int before = carry;
+    for (int q = 0; q < wave; ++q) before += wcnt[q];
+    const int pos = before + __popcll(m & ((1ull << lane) - 1ull));
+    if (bit && pos < topk) selrow[pos] = w;  // more than k only with duplicate ids
+    carry += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+    __syncthreads();
   }
   for (int p = n_sel + t; p < topk; p += 256) selrow[p] = -1;
   if (t == 0) sel_count[bh * QB + i] = n_sel;
@@ -326,12 +347,12 @@ size_t select_ws_bytes(const pbsa_problem &p) {
 }
 
 size_t select_lds_bytes(const pbsa_problem &p) {
-  return (128 + (size_t)p.C + p.W) * sizeof(float) + (size_t)p.W * (sizeof(int) + sizeof(int64_t));
+  return (128 + (size_t)p.C + p.W) * sizeof(float) + (size_t)p.W * (2 * sizeof(int) + sizeof(int64_t));
 }
 
 hipError_t launch_select(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
                          int32_t *sel, int32_t *sel_count, float *mass_pool, float *mass_win,
-                         void *ws, hipStream_t st) {
+                         bool masses, void *ws, hipStream_t st) {
   const int QB = (p.Nq + p.T - 1) / p.T;
   const size_t bh = (size_t)p.B * p.H;
   float *qbar = reinterpret_cast<float *>(ws);
@@ -348,6 +369,16 @@ hipError_t launch_select(const pbsa_problem &p, float scale, const void *q, cons
   score_topk_kernel<<<g2, 256, select_lds_bytes(p), st>>>(
       qbar, kv.kbar_pool, kv.kbar_win, kv.kbar_cur, kv.pool_count, kv.win_len, kv.win_id, sel,
       sel_count, srows, p.H, p.d, p.T, p.W, p.C, QB, p.topk, scale, p.dev_status);
+  if (masses) return launch_block_mass(p, mass_pool, mass_win, ws, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_mass(const pbsa_problem &p, float *mass_pool, float *mass_win,
+                             const void *ws, hipStream_t st) {
+  const int QB = (p.Nq + p.T - 1) / p.T;
+  const size_t bh = (size_t)p.B * p.H;
+  const char *wsb = reinterpret_cast<const char *>(ws);
+  const float *srows = reinterpret_cast<const float *>(wsb + align256(bh * QB * p.d * sizeof(float)));
   if (p.C + p.W > 0)
     block_mass_kernel<<<dim3(p.H, p.B), kMassThreads, 0, st>>>(srows, mass_pool, mass_win, p.H, p.W,
                                                                 p.C, QB);

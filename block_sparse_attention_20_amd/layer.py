@@ -86,11 +86,18 @@ class PBSALayer:
                               self.B * self.H * self.C, self.t["kbar_pool"])
 
     # -- the four calls ------------------------------------------------------
-    def select(self):
+    def select(self, masses: bool = True):
+        """Routing; with masses=False the block masses are left to
+        block_mass() (which reads the scores this call leaves in ws_select)."""
         t = self.t
         P.pbsa_select(self.prob, t["q"], self.kv, t["sel"] if self.topk > 0 else None,
-                      t["sel_count"], t["mass_pool"] if self.C > 0 else None,
-                      t["mass_win"] if self.W > 0 else None, self.ws_select)
+                      t["sel_count"], t["mass_pool"] if masses and self.C > 0 else None,
+                      t["mass_win"] if masses and self.W > 0 else None, self.ws_select)
+
+    def block_mass(self):
+        t = self.t
+        P.pbsa_block_mass(self.prob, t["mass_pool"] if self.C > 0 else None,
+                          t["mass_win"] if self.W > 0 else None, self.ws_select)
 
     def fwd(self, with_lse=True):
         t = self.t

@@ -21,7 +21,7 @@ PBSA_OP_SELECT, PBSA_OP_FWD, PBSA_OP_BWD, PBSA_OP_UPDATE = 0, 1, 2, 3
 PBSA_STATUS_POOL_COUNT, PBSA_STATUS_WIN_LEN, PBSA_STATUS_SEL, PBSA_STATUS_SINK = 1, 2, 4, 8
 
 # every exported symbol declared in include/pbsa.h
-EXPORTS = ("pbsa_select", "pbsa_attn_fwd", "pbsa_attn_bwd", "pbsa_memory_update",
+EXPORTS = ("pbsa_select", "pbsa_block_mass", "pbsa_attn_fwd", "pbsa_attn_bwd", "pbsa_memory_update",
            "pbsa_block_mean", "pbsa_window_append", "pbsa_workspace_size", "pbsa_validate",
            "pbsa_strerror", "pbsa_last_error")
 
@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
         P, K, G = ctypes.POINTER(Problem), ctypes.POINTER(KV), ctypes.POINTER(KVGrad)
         sig = {
             "pbsa_select": (ctypes.c_int, [P, vp, K, vp, vp, vp, vp, vp, sz, vp]),
+            "pbsa_block_mass": (ctypes.c_int, [P, vp, vp, vp, sz, vp]),
             "pbsa_attn_fwd": (ctypes.c_int, [P, vp, K, vp, vp, vp, vp, vp, sz, vp]),
             "pbsa_attn_bwd": (ctypes.c_int, [P, vp, K, vp, vp, vp, vp, vp, vp, G, vp, sz, vp]),
             "pbsa_memory_update": (ctypes.c_int, [P, K, vp, vp, vp, i32, i64, vp, sz, vp]),
@@ -156,6 +157,12 @@ def pbsa_memory_update(prob, kv: KV, mass_pool, mass_win, leaving, n_leave, n_si
                                     _p(mass_win), _p(leaving), int(n_leave), int(n_sink), _p(ws),
                                     0 if ws is None else ws.numel() * ws.element_size(),
                                     _stream(stream)))
+
+
+def pbsa_block_mass(prob, mass_pool, mass_win, ws, stream=None):
+    _check(lib().pbsa_block_mass(ctypes.byref(prob), _p(mass_pool), _p(mass_win), _p(ws),
+                                 0 if ws is None else ws.numel() * ws.element_size(),
+                                 _stream(stream)))
 
 
 def pbsa_block_mean(prob, x, length, n_blocks, out, stream=None):

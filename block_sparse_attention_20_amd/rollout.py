@@ -11,17 +11,19 @@ persistent memory updated by Top-C retention).
 Per layer and chunk t (all device work is libpbsa.so; nothing syncs):
   1. pbsa_select and pbsa_attn_fwd against the window (chunks t-2, t-1) and
      the pool;
-  2. once the window is full (t >= window_chunks), pbsa_memory_update with
-     the slots of chunk t-2 as the leaving blocks;
+  2. once the window is full (t >= window_chunks), the block masses
+     (pbsa_block_mass, or inside pbsa_select without a side stream) and
+     pbsa_memory_update with the slots of chunk t-2 as the leaving blocks;
   3. pbsa_window_append writes chunk t into those slots (ring position
      t mod window_chunks), block ids t*QB + j.
 The state of a layer is plain device tensors (``PBSALayer.t``), so it can be
 saved and restored with ``state_dict`` / ``load_state_dict``.
 
 With ``overlap=True`` steps 2-3 go to a side stream: the next layer needs
-only this layer's output O, while the updated pool and window are needed by
-the next *chunk*.  The side stream waits for the layer's forward (the update
-rewrites pool slots the forward reads); the next chunk's select of the layer
+only this layer's output O, while the masses and the updated pool and window
+are needed by the next *chunk*.  The side stream waits for the layer's
+forward (the update rewrites pool slots the forward reads); the next chunk's
+select of the layer (which rewrites the scores the masses are computed from)
 and the next write of its inputs wait for the side work.  Both streams keep
 the default priority.
 """
@@ -81,7 +83,9 @@ class Rollout:
         L = self.layers[layer]
         t = self.t
         self._wait_side(layer)
-        L.select()
+        # with a side stream the block masses (needed only by the update) are
+        # computed there, off the attention's critical path
+        L.select(masses=self.side is None)
         if attention:
             if fwd_events is not None:
                 fwd_events[0].record()
@@ -100,6 +104,8 @@ class Rollout:
 
     def _side_work(self, L, t):
         if t >= self.window_chunks:
+            if self.side is not None:
+                L.block_mass()
             L.update(self.leaving[t % self.window_chunks], self.n_sink)
         L.append_window(self.first_slot(t), t * self.QB)
 

@@ -132,11 +132,27 @@ typedef struct {
  *   mass_pool / mass_win[j] = sum over query blocks i of softmax_j(s_i.)
  *              (the softmax runs over pool + window + current); 0 for
  *              invalid slots.  These are the scores of the Top-C update.
+ * mass_pool and mass_win are optional as a pair: with both NULL the masses
+ * are not computed here (the attention needs only sel); pbsa_block_mass
+ * computes them later from the scores this call leaves in ws.  Otherwise
+ * mass_pool is required when C > 0 and mass_win when W > 0.
  * Workspace: pbsa_workspace_size(p, PBSA_OP_SELECT) bytes.
  */
 int pbsa_select(const pbsa_problem *p, const void *q, const pbsa_kv *kv, int32_t *sel,
                 int32_t *sel_count, float *mass_pool, float *mass_win, void *ws,
                 size_t ws_bytes, pbsa_stream_t stream);
+
+/*
+ * pbsa_block_mass - the block masses of pbsa_select (same definition and
+ * section) from the coarse scores the last pbsa_select call left in ws
+ * (same problem, ws untouched since), so that a rollout can take them off
+ * the attention's critical path and compute them on the stream that runs the
+ * Top-C update.  mass_pool [B,H,C] required when C > 0, mass_win [B,H,W]
+ * when W > 0 (fp32, written in full).
+ * Workspace: the pbsa_select workspace, read only.
+ */
+int pbsa_block_mass(const pbsa_problem *p, float *mass_pool, float *mass_win, const void *ws,
+                    size_t ws_bytes, pbsa_stream_t stream);
 
 /*
  * pbsa_attn_fwd - hybrid attention (same section: dense attention over the

@@ -93,6 +93,15 @@ def test_entry_points_reject_before_launch():
     assert "o" in L.pbsa_last_error().decode()
     # misaligned pointer
     assert L.pbsa_attn_fwd(ctypes.byref(p), fake + 2, ctypes.byref(kv2), fake, fake, fake, None, None, 0, None) == -4
+    # select: masses are optional only as a pair
+    need = L.pbsa_workspace_size(ctypes.byref(p), P.PBSA_OP_SELECT)
+    assert L.pbsa_select(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, None, fake, need, None) == -1
+    assert L.pbsa_select(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, None, fake, fake, need, None) == -1
+    # block mass: both mass buffers and the select workspace
+    assert L.pbsa_block_mass(ctypes.byref(p), None, fake, fake, need, None) == -1
+    assert L.pbsa_block_mass(ctypes.byref(p), fake, None, fake, need, None) == -1
+    assert L.pbsa_block_mass(ctypes.byref(p), fake, fake, None, 0, None) == -5
+    assert L.pbsa_block_mass(ctypes.byref(p), fake, fake, fake, need - 1, None) == -5
     # select without workspace
     assert L.pbsa_select(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, fake, None, 0, None) == -5
     need = L.pbsa_workspace_size(ctypes.byref(p), P.PBSA_OP_SELECT)

@@ -193,6 +193,24 @@ def test_fwd_split_workspace_needs_no_initialisation():
         assert torch.equal(L.t["o"], ref_o) and torch.equal(L.t["lse"], ref_l)
 
 
+def test_block_mass_later_equals_mass_in_select():
+    """pbsa_select without mass buffers followed by pbsa_block_mass gives
+    the masses of pbsa_select with them, bit for bit, and the same routing."""
+    shape, kw = CASES["bf16_d128_T128_small"]
+    st = syn.make_state(shape, 41, **kw)
+    L = run(shape, st)
+    ref = {k: L.t[k].clone() for k in ("mass_pool", "mass_win", "sel", "sel_count")}
+    for k in ("mass_pool", "mass_win"):
+        L.t[k].fill_(float("nan"))
+    L.select(masses=False)
+    torch.cuda.synchronize()
+    assert torch.isnan(L.t["mass_pool"]).all() and torch.isnan(L.t["mass_win"]).all()
+    assert torch.equal(L.t["sel"], ref["sel"]) and torch.equal(L.t["sel_count"], ref["sel_count"])
+    L.block_mass()
+    torch.cuda.synchronize()
+    assert torch.equal(L.t["mass_pool"], ref["mass_pool"]) and torch.equal(L.t["mass_win"], ref["mass_win"])
+
+
 def test_fwd_deterministic_and_fully_written():
     shape, kw = CASES["bf16_d64_T64_multi"]
     st = syn.make_state(shape, 3, **kw)
