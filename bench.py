@@ -40,8 +40,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # FETCH 14,167 KiB, WRITE 28,304 KiB).  Valid only for the kernel source it
 # was measured on (sha1 over FWD_SOURCES below); reported as null once those
 # sources change.
-FWD_TRAFFIC = {"src_sha1": "3ab3c4adb530afdcf74ddb651d091267d30f2c8e",
-               "fetch_kib": 61757.6, "write_kib": 14259.6,
+FWD_TRAFFIC = {"src_sha1": "f2c938d4e18f56816832dc12720859972fde2307",
+               "fetch_kib": 59750.7, "write_kib": 14259.7,
                "fetch_scale": 28302.0 / 14166.7, "write_scale": 28302.0 / 28304.3}
 
 
