@@ -99,8 +99,6 @@ __device__ __forceinline__ int arrive(unsigned long long *c, uint32_t epoch) {
 
 template <int D, int BT>
 struct FwdLds {
-  uint16_t Kb[2][kTile * D] __attribute__((aligned(1024)));
-  uint16_t Vb[2][kTile * D] __attribute__((aligned(1024)));
   BlockList blist;
   int last;
 };
@@ -110,13 +108,17 @@ struct FwdLds {
 // sum to its partial slot, and the last piece to arrive merges all pieces of
 // the item in workgroup order (so the result does not depend on timing).
 template <int D, int BT>
-__device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh, int wg, int item,
+__device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh, uint16_t *K0,
+                                            uint16_t *K1, uint16_t *V0, uint16_t *V1, int wg, int item,
                                             int j0, int j1) {
   constexpr int NW = BT / 32;  // waves; wave w owns query rows [32w, 32w+32)
   constexpr int TT = kTile;
   using G = DmaGeom<D, TT, NW>;
-  uint16_t (&Kb)[2][TT * D] = sh.Kb;
-  uint16_t (&Vb)[2][TT * D] = sh.Vb;
+  // four separate LDS arrays (not one [2][..] array), so that the compiler
+  // sees that this tile's reads and the next tile's DMA touch different
+  // objects and inserts no wait for the DMA in front of the reads
+  uint16_t *const Kb[2] = {K0, K1};
+  uint16_t *const Vb[2] = {V0, V1};
   BlockList &blist = sh.blist;
   const int i = item % a.QB;
   const size_t bh = item / a.QB;
@@ -407,10 +409,12 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
 template <int D, int BT>
 __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   __shared__ FwdLds<D, BT> sh;
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[kTile * D], K1[kTile * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[kTile * D], V1[kTile * D];
   int wg;
   item_of_block(a, wg);
   if (!a.split) {
-    if (wg < a.n_items) fwd_segment<D, BT>(a, sh, wg, wg, 0, a.NB);
+    if (wg < a.n_items) fwd_segment<D, BT>(a, sh, K0, K1, V0, V1, wg, wg, 0, a.NB);
     return;
   }
   if (wg >= a.G) return;
@@ -419,7 +423,7 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kerne
     const int64_t base = (int64_t)item * a.NB;
     const int j0 = (int)(u0 > base ? u0 - base : 0);
     const int j1 = (int)(u1 - base < a.NB ? u1 - base : a.NB);
-    fwd_segment<D, BT>(a, sh, wg, item, j0, j1);
+    fwd_segment<D, BT>(a, sh, K0, K1, V0, V1, wg, item, j0, j1);
   }
 }
 
