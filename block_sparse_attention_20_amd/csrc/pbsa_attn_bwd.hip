@@ -37,6 +37,8 @@
 #include "pbsa_internal.h"
 #include "pbsa_tiles.h"
 
+#include <type_traits>
+
 namespace pbsa {
 
 struct BwdArgs {
@@ -44,7 +46,7 @@ struct BwdArgs {
   const int32_t *win_len, *pool_len, *pool_count, *sel, *sel_count;
   const float *lse;
   uint16_t *dq, *dk_cur, *dv_cur, *dk_win, *dv_win, *dk_pool, *dv_pool;
-  float *Lp, *Dp;  // [bh][QB*T]: log2(e) lse and -D per query row, zero padded
+  float *LDp;  // [bh][QB*T][2]: (log2(e) lse, -D) per query row, zero padded
   int32_t *qptr, *qidx;
   int32_t *status;
   int H, Nq, W, C, topk, QB, n_items, per_xcd;
@@ -66,8 +68,7 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(const uint16_t *__restrict__ o,
                                                        const uint16_t *__restrict__ dout,
                                                        const float *__restrict__ lse,
-                                                       float *__restrict__ Lp,
-                                                       float *__restrict__ Dp, size_t rows_p,
+                                                       float *__restrict__ LDp, size_t rows_p,
                                                        int Nq, int NqP) {
   constexpr int TPR = D / 8;  // threads per row
   const size_t rp = (size_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
@@ -86,8 +87,8 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const uint16_t *__restric
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (rp < rows_p && c == 0) {
-    Dp[rp] = -acc;
-    Lp[rp] = ok ? lse[src] * kLog2e : 0.f;
+    LDp[2 * rp] = ok ? lse[src] * kLog2e : 0.f;
+    LDp[2 * rp + 1] = -acc;
   }
 }
 
@@ -271,17 +272,14 @@ __global__ __launch_bounds__(256) void bwd_csr_kernel(const int32_t *__restrict_
 // over a [64][D] tile swizzled with kSwzU: for 16 tile rows starting at a
 // multiple of 16, lane (gi = lane & 15) of each 16-lane group addresses row
 // 4g + gi/4 (lo) and the row 8 further (hi), dims 32 dt + 16 q16 + 4 (gi & 3).
+// Because the swizzle XORs whole chunks, the offsets of dims tile dt are the
+// dt = 0 offset XOR 32 dt, and the hi row's is the lo one XOR 16 plus 8 rows:
+// one base per lane (tr_base) and two XORs per fragment (tr_frag_u).
 template <int D>
-__device__ __forceinline__ void tr_offsets(int lane, int (&lo)[D / 32], int (&hi)[D / 32]) {
+__device__ __forceinline__ int tr_base(int lane) {
   const int g = lane >> 5, gi = lane & 15, q16 = (lane >> 4) & 1, vr = gi >> 2, vq = gi & 3;
-  const int rlo = 4 * g + vr, rhi = rlo + 8;
-  const int slo = lds_swz<D, kSwzU>(rlo), shi = lds_swz<D, kSwzU>(rhi);
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    const int c = 4 * dt + 2 * q16 + (vq >> 1);
-    lo[dt] = rlo * D + ((c ^ slo) * 8) + (vq & 1) * 4;
-    hi[dt] = rhi * D + ((c ^ shi) * 8) + (vq & 1) * 4;
-  }
+  const int rlo = 4 * g + vr;
+  return rlo * D + (((2 * q16 + (vq >> 1)) ^ lds_swz<D, kSwzU>(rlo)) * 8) + (vq & 1) * 4;
 }
 
 __device__ __forceinline__ bf16x8 tr_read(const uint16_t *tile, int lo, int hi) {
@@ -289,6 +287,12 @@ __device__ __forceinline__ bf16x8 tr_read(const uint16_t *tile, int lo, int hi) 
   const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&tile[hi]));
   return __builtin_bit_cast(bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){
                                         x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]});
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag_u(const uint16_t *tile, int base, int dt) {
+  const int lo = base ^ (32 * dt);
+  return tr_read(tile, lo, (lo ^ 16) + 8 * D);
 }
 
 // this lane's row as MFMA B fragments (dims 16 kk + 8 g .. + 7)
@@ -332,8 +336,8 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dq_kernel(BwdAr
     load_bfrag<D>(df, a.dout + base, qok, g);
   }
   const size_t prow = bh * (size_t)(a.QB * BT) + qrow;
-  const float Lq = a.Lp[prow];
-  const float Dn = a.Dp[prow];  // -D of this query row
+  const float Lq = a.LDp[2 * prow];
+  const float Dn = a.LDp[2 * prow + 1];  // -D of this query row
   const float sl2 = a.sl2;
   f32x16 dqacc[D / 32];
 #pragma unroll
@@ -351,8 +355,7 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dq_kernel(BwdAr
       voff[kk] = l32 * D + (((2 * kk + g) ^ vs) * 8);
     }
   }
-  int tlo[D / 32], thi[D / 32];
-  tr_offsets<D>(lane, tlo, thi);
+  const int tbase = tr_base<D>(lane);
   uint32_t kdma[G::NVAR], vdma[G::NVAR];
   dma_lane_offsets<D, TT, NW, kSwzU>(lane, kdma);
   dma_lane_offsets<D, TT, NW, kSwzK>(lane, vdma);
@@ -364,8 +367,8 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dq_kernel(BwdAr
   int blen;
   list_block<D, BT>(a, blist, bh, i, n_pool, sc, 0, kb, vb, blen);
   int tlen = min(TT, blen);
-  dma_block<D, TT, NW, kSwzU>(Kb[0], kb, tlen, wave, lane, kdma);
-  dma_block<D, TT, NW, kSwzK>(Vb[0], vb, tlen, wave, lane, vdma);
+  TileDma<D, TT, NW>::tile(Kb[0], kb, tlen, wave, kdma);
+  TileDma<D, TT, NW>::tile(Vb[0], vb, tlen, wave, vdma);
   int buf = 0;
 
   while (true) {
@@ -382,8 +385,8 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dq_kernel(BwdAr
     const bool more = jn < nb;
     if (more) {
       nlen = min(TT, bn - hn * TT);
-      dma_block<D, TT, NW, kSwzU>(Kb[buf ^ 1], kn + hn * TT * D, nlen, wave, lane, kdma);
-      dma_block<D, TT, NW, kSwzK>(Vb[buf ^ 1], vn + hn * TT * D, nlen, wave, lane, vdma);
+      TileDma<D, TT, NW>::tile(Kb[buf ^ 1], kn + hn * TT * D, nlen, wave, kdma);
+      TileDma<D, TT, NW>::tile(Vb[buf ^ 1], vn + hn * TT * D, nlen, wave, vdma);
     }
     const uint16_t *Kl = Kb[buf];
     const uint16_t *Vl = Vb[buf];
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dq_kernel(BwdAr
           const uint16_t *Kst = Kl + (2 * hf + hh) * 16 * D;
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt)
-            dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(Kst, tlo[dt], thi[dt]), sf,
+            dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_u<D>(Kst, tbase, dt), sf,
                                                                 dqacc[dt], 0, 0, 0);
         }
       }
@@ -458,13 +461,13 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dq_kernel(BwdAr
 //    [pool C | current QB | window W].
 // ---------------------------------------------------------------------------
 
-// L and D of query rows [r0, r0 + 64) into LD[0..63] and LD[64..127] with one
-// 1 KB DMA by wave 0 (lanes 32..63 fill LD[128..255] from the zero page).
-__device__ __forceinline__ void dma_rows_ld(float *LD, const float *L, const float *Dv, int lane) {
-  const char *g = lane < 16   ? reinterpret_cast<const char *>(L + 4 * lane)
-                  : lane < 32 ? reinterpret_cast<const char *>(Dv + 4 * (lane - 16))
-                              : reinterpret_cast<const char *>(g_zero_rows + 4 * (lane & 15));
-  __builtin_amdgcn_global_load_lds(g, (lds_void *)LD, 16, 0, 0);
+// (L, -D) of query rows [r0, r0 + 64) into LD[0..127] (row r at 2r, 2r+1)
+// with one 1 KB buffer load by wave 0: lanes 0..31 move the 512 bytes, lanes
+// 32..63 are past the descriptor's range and write zeros to LD[128..255].
+__device__ __forceinline__ void dma_rows_ld(float *LD, const float *src, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(src), (short)0, 512, 0x00020000),
+      (lds_void *)LD, 16, (uint32_t)lane * 16, 0, 0, 0);
 }
 
 template <int D, int BT>
@@ -473,7 +476,7 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dkv_kernel(BwdA
   using G = DmaGeom<D, TT, NW>;
   __shared__ __attribute__((aligned(1024))) uint16_t Qb[2][TT * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Ob[2][TT * D];  // dO rows
-  __shared__ __attribute__((aligned(1024))) float LD[2][256];
+  __shared__ __attribute__((aligned(1024))) float LD[2][256];  // (L, -D) per row, 128..255 zero
   const int item = bwd_item(a);
   if (item >= a.n_items) return;
   const int nj = a.C + a.W + a.QB;
@@ -529,8 +532,7 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dkv_kernel(BwdA
     // A = Q / dO rows: tile row 32 qs + l32, logical chunk 2 kk + g
     // (chunk 2 kk + g) ^ s = (g ^ s) ^ 2 kk: one base offset, XOR 16 kk per step
     const int rbase = l32 * D + ((g ^ lds_swz<D, kSwzU>(l32)) * 8);
-    int tlo[D / 32], thi[D / 32];
-    tr_offsets<D>(lane, tlo, thi);
+    const int tbase = tr_base<D>(lane);
     uint32_t rdma[G::NVAR];
     dma_lane_offsets<D, TT, NW, kSwzU>(lane, rdma);
     const size_t NqP = (size_t)a.QB * BT;
@@ -542,9 +544,9 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dkv_kernel(BwdA
     int tlen = min(TT, qlen);
     {
       const size_t r0 = bh * a.Nq + (size_t)qi * BT;
-      dma_block<D, TT, NW, kSwzU>(Qb[0], a.q + r0 * D, tlen, wave, lane, rdma);
-      dma_block<D, TT, NW, kSwzU>(Ob[0], a.dout + r0 * D, tlen, wave, lane, rdma);
-      if (wave == 0) dma_rows_ld(LD[0], a.Lp + bh * NqP + qi * BT, a.Dp + bh * NqP + qi * BT, lane);
+      TileDma<D, TT, NW>::tile(Qb[0], a.q + r0 * D, tlen, wave, rdma);
+      TileDma<D, TT, NW>::tile(Ob[0], a.dout + r0 * D, tlen, wave, rdma);
+      if (wave == 0) dma_rows_ld(LD[0], a.LDp + 2 * (bh * NqP + qi * BT), lane);
     }
     int buf = 0;
     while (true) {
@@ -563,17 +565,13 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dkv_kernel(BwdA
       if (more) {
         nlen = min(TT, qlenn - hn * TT);
         const size_t r0 = bh * a.Nq + (size_t)qin * BT + hn * TT;
-        dma_block<D, TT, NW, kSwzU>(Qb[buf ^ 1], a.q + r0 * D, nlen, wave, lane, rdma);
-        dma_block<D, TT, NW, kSwzU>(Ob[buf ^ 1], a.dout + r0 * D, nlen, wave, lane, rdma);
-        if (wave == 0) {
-          const size_t p0 = bh * NqP + (size_t)qin * BT + hn * TT;
-          dma_rows_ld(LD[buf ^ 1], a.Lp + p0, a.Dp + p0, lane);
-        }
+        TileDma<D, TT, NW>::tile(Qb[buf ^ 1], a.q + r0 * D, nlen, wave, rdma);
+        TileDma<D, TT, NW>::tile(Ob[buf ^ 1], a.dout + r0 * D, nlen, wave, rdma);
+        if (wave == 0) dma_rows_ld(LD[buf ^ 1], a.LDp + 2 * (bh * NqP + (size_t)qin * BT + hn * TT), lane);
       }
       const uint16_t *Ql = Qb[buf];
       const uint16_t *Ol = Ob[buf];
-      const float *Ll = LD[buf];
-      const float *Dl = LD[buf] + 64;
+      const float *LDl = LD[buf];
 
 #pragma unroll 1
       for (int qs = 0; qs < TT / 32; ++qs) {
@@ -585,12 +583,12 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dkv_kernel(BwdA
           f32x16 sacc, pacc;
 #pragma unroll
           for (int m4 = 0; m4 < 4; ++m4) {
-            const f32x4 D4 = *reinterpret_cast<const f32x4 *>(&Dl[qs * 32 + 8 * m4 + 4 * g]);
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-              sacc[4 * m4 + e4] = 0.f;
-              pacc[4 * m4 + e4] = D4[e4];
-            }
+            const int r = qs * 32 + 8 * m4 + 4 * g;  // rows r .. r+3: (L, -D) pairs
+            sacc[4 * m4] = sacc[4 * m4 + 1] = sacc[4 * m4 + 2] = sacc[4 * m4 + 3] = 0.f;
+            pacc[4 * m4] = LDl[2 * r + 1];  // (scalar reads: fewer live registers
+            pacc[4 * m4 + 1] = LDl[2 * r + 3];  //  than two 16-byte reads)
+            pacc[4 * m4 + 2] = LDl[2 * r + 5];
+            pacc[4 * m4 + 3] = LDl[2 * r + 7];
           }
 #pragma unroll
           for (int kk = 0; kk < D / 16; ++kk) {
@@ -604,7 +602,10 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dkv_kernel(BwdA
           // so they contribute nothing (P = 1, dS = 0 there).
 #pragma unroll
           for (int m4 = 0; m4 < 4; ++m4) {
-            const f32x4 L4 = *reinterpret_cast<const f32x4 *>(&Ll[qs * 32 + 8 * m4 + 4 * g]);
+            const int r = qs * 32 + 8 * m4 + 4 * g;
+            const f32x4 lo = *reinterpret_cast<const f32x4 *>(&LDl[2 * r]);
+            const f32x4 hi = *reinterpret_cast<const f32x4 *>(&LDl[2 * r + 4]);
+            const float L4[4] = {lo[0], lo[2], hi[0], hi[2]};
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4) {
               const int e = 4 * m4 + e4;
@@ -625,9 +626,9 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dkv_kernel(BwdA
             const int st = (2 * qs + hh) * 16 * D;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
-              dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(Ol + st, tlo[dt], thi[dt]), pf,
+              dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_u<D>(Ol + st, tbase, dt), pf,
                                                                   dvacc[dt], 0, 0, 0);
-              dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(Ql + st, tlo[dt], thi[dt]), sf,
+              dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_u<D>(Ql + st, tbase, dt), sf,
                                                                   dkacc[dt], 0, 0, 0);
             }
           }
@@ -674,7 +675,7 @@ size_t bwd_ws_bytes(const pbsa_problem &p) {
   const size_t bh = (size_t)p.B * p.H;
   const size_t QB = (p.Nq + p.T - 1) / p.T;
   const size_t rows_p = bh * QB * p.T;
-  return 2 * align256(rows_p * sizeof(float)) + align256(bh * (p.W + 1) * sizeof(int32_t)) +
+  return align256(2 * rows_p * sizeof(float)) + align256(bh * (p.W + 1) * sizeof(int32_t)) +
          align256(bh * QB * (size_t)(p.topk > 0 ? p.topk : 1) * sizeof(int32_t));
 }
 
@@ -703,10 +704,8 @@ hipError_t launch_attn_bwd(const pbsa_problem &p, float scale, const void *q, co
   const size_t bh = (size_t)p.B * p.H;
   const size_t rows_p = bh * a.QB * p.T;
   char *w = reinterpret_cast<char *>(ws);
-  a.Lp = reinterpret_cast<float *>(w);
-  w += align256(rows_p * sizeof(float));
-  a.Dp = reinterpret_cast<float *>(w);
-  w += align256(rows_p * sizeof(float));
+  a.LDp = reinterpret_cast<float *>(w);
+  w += align256(2 * rows_p * sizeof(float));
   a.qptr = reinterpret_cast<int32_t *>(w);
   w += align256(bh * (p.W + 1) * sizeof(int32_t));
   a.qidx = reinterpret_cast<int32_t *>(w);
@@ -715,9 +714,9 @@ hipError_t launch_attn_bwd(const pbsa_problem &p, float scale, const void *q, co
   const unsigned rblocks = (unsigned)((rows_p + rpb - 1) / rpb);
   const int NqP = a.QB * p.T;
   if (p.d == 128)
-    bwd_rows_kernel<128><<<rblocks, 256, 0, st>>>(a.o, a.dout, lse, a.Lp, a.Dp, rows_p, p.Nq, NqP);
+    bwd_rows_kernel<128><<<rblocks, 256, 0, st>>>(a.o, a.dout, lse, a.LDp, rows_p, p.Nq, NqP);
   else
-    bwd_rows_kernel<64><<<rblocks, 256, 0, st>>>(a.o, a.dout, lse, a.Lp, a.Dp, rows_p, p.Nq, NqP);
+    bwd_rows_kernel<64><<<rblocks, 256, 0, st>>>(a.o, a.dout, lse, a.LDp, rows_p, p.Nq, NqP);
   if (p.W > 0 && p.topk > 0) {
     if ((int64_t)a.QB * p.W <= kCsrMat)
       bwd_csr_mat_kernel<<<dim3(p.H, p.B), 256, 0, st>>>(sel, sel_count, a.qptr, a.qidx, p.H, p.W,

@@ -11,10 +11,11 @@
 // workgroups per CU (64 KB LDS and <= 256 VGPRs each):
 //   - T/32 waves, wave w owns query rows [32w, 32w+32) of the block;
 //   - the block list (pool, selected window slots, current chunk) is walked
-//     in order.  K and V of a block are moved HBM -> LDS by
-//     global_load_lds_dwordx4 (no register round trip) into row-major tiles
-//     whose 16-byte chunks are XOR-swizzled per row; rows past the valid
-//     length come from a zero page, so padding can never inject NaN;
+//     in order.  K and V of a block are moved HBM -> LDS by raw buffer loads
+//     with the LDS flag (no register round trip) into row-major tiles whose
+//     16-byte chunks are XOR-swizzled per row; each buffer descriptor covers
+//     only the valid rows, so lanes past them write zeros and padding can
+//     never inject NaN;
 //   - the next block's K is in flight while the softmax and P V of the
 //     current block run, and its V while the next S is computed (one K and
 //     one V buffer, four barriers per block);
@@ -180,8 +181,8 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
   if (j0 < jend) {
     list_block<D, BT>(a, blist, bh, i, n_pool, sc, j0, kb, vb, blen);
     tlen = min(TT, blen);
-    dma_block<D, TT, NW, kSwzK>(Kb[0], kb, tlen, wave, lane, kdma);
-    dma_block<D, TT, NW, kSwzV>(Vb[0], vb, tlen, wave, lane, vdma);
+    TileDma<D, TT, NW>::tile(Kb[0], kb, tlen, wave, kdma);
+    TileDma<D, TT, NW>::tile(Vb[0], vb, tlen, wave, vdma);
   }
   // the two LDS buffers alternate; each is a compile-time index so that
   // tile addresses are immediate offsets
@@ -199,20 +200,14 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
       if (jn < jend) list_block<D, BT>(a, blist, bh, i, n_pool, sc, jn, kn, vn, bn);
     }
     const bool more = jn < jend;
-    // the next tile's DMA: a ragged tile is issued here; a full one is
-    // spread over the k-steps of S below, between the MFMAs
-    bool dfull = false;
-    const char *kd = nullptr, *vd = nullptr;
+    // the next tile's DMA is spread over the k-steps of S below, between
+    // the MFMAs (issued as one burst it stalls the wave on the vector-memory
+    // queue); its descriptors cover the valid rows only
+    TileSrc<D, TT, NW> ksrc, vsrc;
     if (more) {
       nlen = min(TT, bn - hn * TT);
-      if (nlen < TT) {
-        dma_block<D, TT, NW, kSwzK>(Kb[buf ^ 1], kn + hn * TT * D, nlen, wave, lane, kdma);
-        dma_block<D, TT, NW, kSwzV>(Vb[buf ^ 1], vn + hn * TT * D, nlen, wave, lane, vdma);
-      } else {
-        dfull = true;
-        kd = dma_wave_src<D, TT, NW>(kn + hn * TT * D, wave);
-        vd = dma_wave_src<D, TT, NW>(vn + hn * TT * D, wave);
-      }
+      ksrc = TileDma<D, TT, NW>::src(kn + hn * TT * D, nlen, wave);
+      vsrc = TileDma<D, TT, NW>::src(vn + hn * TT * D, nlen, wave);
     }
     const uint16_t *Kl = Kb[buf];
     const uint16_t *Vl = Vb[buf];
@@ -240,15 +235,15 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
         }
         // this k-step's share of the next tile's DMA (2 IPW instructions
         // over D/16 steps)
-        if (dfull) {
+        if (more) {
           constexpr int NI = 2 * G::IPW, PER = (NI + D / 16 - 1) / (D / 16);
 #pragma unroll
           for (int q = 0; q < PER; ++q) {
             const int it2 = kk * PER + q;
             if (it2 < G::IPW)
-              dma_one<D, TT, NW>(Kb[buf ^ 1], kd, wave, it2, kdma);
+              TileDma<D, TT, NW>::one(Kb[buf ^ 1], ksrc, wave, it2, kdma);
             else if (it2 < NI)
-              dma_one<D, TT, NW>(Vb[buf ^ 1], vd, wave, it2 - G::IPW, vdma);
+              TileDma<D, TT, NW>::one(Vb[buf ^ 1], vsrc, wave, it2 - G::IPW, vdma);
           }
         }
 #pragma unroll

@@ -11,11 +11,6 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // s_waitcnt immediate: vmcnt <= n, expcnt and lgkmcnt unconstrained (gfx9 encoding)
 #define PBSA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14)))
 
-// 256 bytes of zeros: the DMA source for rows past a block's valid length
-// (padding rows and the tail of the last current block), so that they land
-// in LDS as zeros without a register round trip.
-static __device__ __attribute__((aligned(256))) uint32_t g_zero_rows[64];
-
 // LDS swizzles (gfx950 LDS: 64 banks of 4 bytes; a 16-byte read serves 16
 // lanes per cycle, an 8-byte read 32 lanes).  Rows are 16-byte chunks; the
 // physical chunk of logical chunk c in row r is c ^ swz(r).
@@ -37,20 +32,27 @@ __device__ __forceinline__ int lds_swz(int r) {
   else return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
-// Stage one [BT][D] bf16 block (rows >= len read as zeros) into LDS,
+// Stage one [BT][D] bf16 tile (rows >= valid read as zeros) into LDS,
 // swizzled as above.  Each wave moves IPW chunks of 1 KB with
-// global_load_lds_dwordx4 (lane l lands at base + 16 l), so the whole block
-// is in flight without touching VGPRs.  Instruction `it` of a wave covers
-// rows row0 + it*RPI + lane/CPR; every wave's first row is a multiple of 16,
-// so a lane's source offset within its row band repeats every 16/RPI
-// instructions: dma_lane_offsets() computes those few byte offsets once.
+// buffer_load_dwordx4 ... lds (lane l lands at base + 16 l), so the whole
+// tile is in flight without touching VGPRs.  The source is a buffer
+// descriptor over the tile's valid rows only: a lane whose row is past the
+// end is out of range and writes zeros, so padding rows never reach the
+// MFMAs (and NaN padding in HBM cannot leak).  Instruction `it` of a wave
+// covers rows row0 + it*RPI + lane/CPR; every wave's first row is a multiple
+// of 16, so a lane's offset within its 16-row band repeats every 16/RPI
+// instructions: dma_lane_offsets() computes those few byte offsets once, and
+// each band gets its own descriptor (group), so the per-instruction offset
+// is a fixed VGPR and the rest is scalar.
 template <int D, int BT, int NW>
 struct DmaGeom {
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;          // rows per 1 KB instruction
   static constexpr int IPW = BT * D * 2 / 1024 / NW;
   static constexpr int NVAR = 16 / RPI < IPW ? 16 / RPI : IPW;  // distinct lane offsets
+  static constexpr int NGRP = IPW / NVAR;       // 16-row bands per wave
   static_assert((IPW * RPI) % 16 == 0, "wave row ranges must start at multiples of 16");
+  static_assert(IPW % NVAR == 0, "whole bands per wave");
 };
 
 template <int D, int BT, int NW, int MODE>
@@ -64,55 +66,59 @@ __device__ __forceinline__ void dma_lane_offsets(int lane, uint32_t (&ofs)[DmaGe
   }
 }
 
-// Ragged block (len < BT): rows past len come from the zero page.
+// One wave's bands of a tile: rows [0, valid) of `src`; band grp starts at
+// row wave * IPW * RPI + 16 grp and may read `bytes` bytes from there.
+// (Plain pointers and sizes; the buffer descriptors are formed where they
+// are used, in scalar registers.)
 template <int D, int BT, int NW>
-__device__ __forceinline__ void dma_block_ragged(uint16_t *dst, const char *base, int row0,
-                                                          int len, int lane,
-                                                          const uint32_t *ofs) {
-  using G = DmaGeom<D, BT, NW>;
-  const int rsub = lane / G::CPR, p = lane % G::CPR;
-#pragma unroll
-  for (int it = 0; it < G::IPW; ++it) {
-    const bool ok = row0 + it * G::RPI + rsub < len;
-    const char *g = ok ? base + (it / G::NVAR) * (G::NVAR * G::RPI * D * 2) + ofs[it % G::NVAR]
-                       : reinterpret_cast<const char *>(g_zero_rows + p * 4);
-    __builtin_amdgcn_global_load_lds(g, (lds_void *)(dst + it * 512), 16, 0, 0);
-  }
-}
+struct TileSrc {
+  const uint16_t *base[DmaGeom<D, BT, NW>::NGRP];
+  int bytes[DmaGeom<D, BT, NW>::NGRP];
+};
 
-template <int D, int BT, int NW, int MODE>
-__device__ __forceinline__ void dma_block(uint16_t *lds, const uint16_t *src, int len, int wave,
-                                          int lane, const uint32_t (&ofs)[DmaGeom<D, BT, NW>::NVAR]) {
+template <int D, int BT, int NW>
+struct TileDma {
   using G = DmaGeom<D, BT, NW>;
-  const int row0 = wave * G::IPW * G::RPI;
-  const char *base = reinterpret_cast<const char *>(src + (size_t)row0 * D);
-  uint16_t *dst = lds + wave * G::IPW * 512;
-  if (len >= BT) {
+
+  // `p` and `valid` are the same in every lane of the wave; reading them
+  // from the first lane says so to the compiler, which then keeps the
+  // descriptors in scalar registers instead of looping over lane values.
+  __device__ static __forceinline__ TileSrc<D, BT, NW> src(const uint16_t *p, int valid, int wave) {
+    const uint64_t pu = reinterpret_cast<uint64_t>(p);
+    p = reinterpret_cast<const uint16_t *>(
+        (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)pu) |
+        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(pu >> 32)) << 32));
+    valid = __builtin_amdgcn_readfirstlane(valid);
+    TileSrc<D, BT, NW> t;
 #pragma unroll
-    for (int it = 0; it < G::IPW; ++it) {
-      const char *g = base + (it / G::NVAR) * (G::NVAR * G::RPI * D * 2) + ofs[it % G::NVAR];
-      __builtin_amdgcn_global_load_lds(g, (lds_void *)(dst + it * 512), 16, 0, 0);
+    for (int grp = 0; grp < G::NGRP; ++grp) {
+      const int row0 = wave * G::IPW * G::RPI + grp * 16;
+      t.base[grp] = p + (size_t)row0 * D;
+      t.bytes[grp] = valid > row0 ? (valid - row0) * D * 2 : 0;
     }
-  } else {
-    dma_block_ragged<D, BT, NW>(dst, base, row0, len, lane, ofs);
+    return t;
   }
-}
 
-// The same full-tile DMA one instruction at a time, so that a kernel can
-// spread a tile's loads between its MFMAs: `wsrc` is the block's first row
-// of this wave's share (src + wave * IPW * RPI rows), `it` < IPW.
-template <int D, int BT, int NW>
-__device__ __forceinline__ void dma_one(uint16_t *lds, const char *wsrc, int wave, int it,
-                                        const uint32_t *ofs) {
-  using G = DmaGeom<D, BT, NW>;
-  const char *g = wsrc + (it / G::NVAR) * (G::NVAR * G::RPI * D * 2) + ofs[it % G::NVAR];
-  __builtin_amdgcn_global_load_lds(g, (lds_void *)(lds + wave * G::IPW * 512 + it * 512), 16, 0, 0);
-}
-template <int D, int BT, int NW>
-__device__ __forceinline__ const char *dma_wave_src(const uint16_t *src, int wave) {
-  using G = DmaGeom<D, BT, NW>;
-  return reinterpret_cast<const char *>(src + (size_t)wave * G::IPW * G::RPI * D);
-}
+  // Instruction `it` (< IPW) of this wave's share of a tile: a raw buffer
+  // load (stride 0) whose descriptor covers the band's valid bytes, so lanes
+  // past them write zeros.
+  __device__ static __forceinline__ void one(uint16_t *lds, const TileSrc<D, BT, NW> &t, int wave,
+                                             int it, const uint32_t *ofs) {
+    const int grp = it / G::NVAR;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(t.base[grp]), (short)0, t.bytes[grp],
+                                          0x00020000),
+        (lds_void *)(lds + wave * G::IPW * 512 + it * 512), 16, ofs[it % G::NVAR], 0, 0, 0);
+  }
+
+  // The whole tile: rows [0, valid) of `p`, zeros after.
+  __device__ static __forceinline__ void tile(uint16_t *lds, const uint16_t *p, int valid, int wave,
+                                              const uint32_t *ofs) {
+    const TileSrc<D, BT, NW> t = src(p, valid, wave);
+#pragma unroll
+    for (int it = 0; it < G::IPW; ++it) one(lds, t, wave, it, ofs);
+  }
+};
 
 // A = V^T / K^T / Q^T fragment of a 32x32x16 MFMA read from a row-major
 // [rows][D] tile with ds_read_b64_tr_b16: two 4-row bands (rows r1 and
