@@ -108,6 +108,13 @@ struct FwdLds {
 // writes O and LSE; a piece writes its unnormalised O^T, running max and row
 // sum to its partial slot, and the last piece to arrive merges all pieces of
 // the item in workgroup order (so the result does not depend on timing).
+// max of x over lanes l and l ^ 32 (v_permlane32_swap exchanges the two
+// lane halves of a register; no LDS round trip)
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <int D, int BT>
 __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh, uint16_t *K0,
                                             uint16_t *K1, uint16_t *V0, uint16_t *V1, int wg, int item,
@@ -148,7 +155,9 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
-  float m = -INFINITY, l = 0.f;  // running max (log2 units) and row sum
+  // running max (log2 units) and row sum, the sum as four partial sums so
+  // that the adds of a tile are not one dependent chain
+  float m = -INFINITY, l4[4] = {0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.sl2;
 
   // Per-lane LDS element offsets, fixed for the whole kernel.
@@ -202,13 +211,12 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
     const bool more = jn < jend;
     // the next tile's DMA is spread over the k-steps of S below, between
     // the MFMAs (issued as one burst it stalls the wave on the vector-memory
-    // queue); its descriptors cover the valid rows only
-    TileSrc<D, TT, NW> ksrc, vsrc;
-    if (more) {
-      nlen = min(TT, bn - hn * TT);
-      ksrc = TileDma<D, TT, NW>::src(kn + hn * TT * D, nlen, wave);
-      vsrc = TileDma<D, TT, NW>::src(vn + hn * TT * D, nlen, wave);
-    }
+    // queue); its descriptors cover the valid rows only.  After the last
+    // tile they cover nothing: the loads then only write zeros into the idle
+    // buffer, which keeps the k-step loop free of branches.
+    if (more) nlen = min(TT, bn - hn * TT);
+    const TileSrc<D, TT, NW> ksrc = TileDma<D, TT, NW>::src(kn + hn * TT * D, nlen, wave);
+    const TileSrc<D, TT, NW> vsrc = TileDma<D, TT, NW>::src(vn + hn * TT * D, nlen, wave);
     const uint16_t *Kl = Kb[buf];
     const uint16_t *Vl = Vb[buf];
 
@@ -235,7 +243,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
         }
         // this k-step's share of the next tile's DMA (2 IPW instructions
         // over D/16 steps)
-        if (more) {
+        {
           constexpr int NI = 2 * G::IPW, PER = (NI + D / 16 - 1) / (D / 16);
 #pragma unroll
           for (int q = 0; q < PER; ++q) {
@@ -265,17 +273,22 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
           if (tok >= tlen) sacc[tt][e] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // row max: four independent chains, then the two lane halves (which
+    // hold the two 4-token interleaves of the same query column) combined
+    // by one lane-half swap
+    float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int tt = 0; tt < TT / 32; ++tt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[tt][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+      for (int e = 0; e < 16; ++e) mc[(2 * tt + (e >> 3)) & 3] = fmaxf(mc[(2 * tt + (e >> 3)) & 3], sacc[tt][e]);
+    float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
+    mx = half_swap_max(mx) * sl2;
     if (__ballot(mx > m + 8.f)) {
       const float mnew = fmaxf(m, mx);
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // m = -inf -> 0
       m = mnew;
-      l *= alpha;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) l4[k] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -305,7 +318,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float p = __builtin_amdgcn_exp2f(sacc[tt][8 * hh + e] * sl2 - muse);
-          l += p;
+          l4[st & 3] += p;
           pf[e] = static_cast<__bf16>(p);
         }
 #pragma unroll
@@ -322,10 +335,12 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
     tlen = nlen;
     return true;
   };
-  if (j0 < jend)
+  if (j0 < jend) {
     while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
     }
-
+    PBSA_WAIT_VM(0);  // the empty loads after the last tile have landed
+  }
+  float l = (l4[0] + l4[1]) + (l4[2] + l4[3]);
   l += __shfl_xor(l, 32);
   if (j0 > 0 || j1 < a.NB) {
     // piece of a split item: publish it, and merge if it is the last one
