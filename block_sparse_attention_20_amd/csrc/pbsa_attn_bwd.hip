@@ -405,6 +405,9 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dq_kernel(BwdAr
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc, 0, 0, 0);
           pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[kk], pacc, 0, 0, 0);
         }
+        // the exponentials and dQ MFMAs run at raised wave priority (as in
+        // the forward: the other workgroup's S / dP MFMAs fill around them)
+        __builtin_amdgcn_s_setprio(1);
         // dS^T = P^T (dP^T - D); tokens past the tile's length (only in the
         // ragged last tile of a block) get P = 0
         if (tlen >= hf * 32 + 32) {
@@ -431,6 +434,7 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dq_kernel(BwdAr
             dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_u<D>(Kst, tbase, dt), sf,
                                                                 dqacc[dt], 0, 0, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
       }
     }
     if (!more) break;

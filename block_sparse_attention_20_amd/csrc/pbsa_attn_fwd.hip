@@ -262,6 +262,12 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
         }
       }
     }
+    // The softmax and P V part of a tile (exponentials interleaved with
+    // MFMAs) runs at raised wave priority: of the two waves sharing a SIMD
+    // (one per workgroup), the one in this part issues first, and the other
+    // one's S MFMAs fill the matrix pipe around it (measured: 7% faster than
+    // equal priorities).
+    __builtin_amdgcn_s_setprio(1);
     // ---- online softmax (log2 domain); the running max only moves when a
     // tile raises it by more than 8, so O is rarely rescaled and P <= 2^8.
     if (tlen < TT) {
@@ -326,6 +332,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st & 1][dt], pf, oacc[dt], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (!more) return false;
     j = jn;
     h = hn;
