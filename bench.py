@@ -246,6 +246,69 @@ def cpu_baseline(ro, budget_s, torch):
                       f"pairs ({t_fwd:.1f} s); value = forward FLOPs / forward time"}
 
 
+def sweep(torch, device="cuda", reps=3, iters=10):
+    """Forward time of the Wan-shaped chunk (12 heads x 128, 4680 tokens,
+    blocks of 128) across sparsity and history length, against the same
+    kernel at its dense limit (every window block selected, no pool).
+
+    - topk axis: window of 2 chunks (74 slots), pool 32, k in {9, 18, 37, 74}
+      (k = 74 is dense over the window);
+    - pool axis: window 74, k = 16, pool in {0, 16, 32, 64};
+    - history axis: h previous chunks; dense attends all 37 h history blocks
+      (W = 37 h, k = W, pool 0); PBSA attends a 2-chunk window (k = 16) and a
+      pool holding the blocks that left the window, capped at 64.
+    """
+    import pbsa_synth as syn
+    from block_sparse_attention_20_amd.layer import PBSALayer
+    from block_sparse_attention_20_amd.rollout import attended_tokens
+    base = syn.WAN_CHUNK
+    qb = base.QB
+
+    def fwd_time(W, C, topk, seed):
+        shape = syn.Shape(B=1, H=base.H, d=base.d, T=base.T, Nq=base.Nq, W=W, C=C, topk=topk)
+        nch = max(1, (W + qb - 1) // qb)
+        wl = (syn.chunk_window_lens(base.Nq, base.T, nch) + [base.T] * W)[:W]
+        st = syn.make_state(shape, seed, sigma=1 / math.sqrt(base.d), shift=1.5,
+                            n_planted=min(8, W), win_len=wl, device=device)
+        L = PBSALayer(shape.B, shape.H, shape.d, shape.T, shape.Nq, W, C, topk, device=device).load(st)
+        del st
+        L.select()
+        for _ in range(3):
+            L.fwd()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(iters):
+                L.fwd()
+            b.record()
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b) * 1e3 / iters)
+        pairs = attended_tokens(L)
+        del L
+        torch.cuda.empty_cache()
+        return {"W": W, "pool": C, "topk": topk, "fwd_us": round(best, 1),
+                "keys_per_query": round(pairs / (base.H * base.Nq), 1),
+                "tflops": round(4 * base.d * pairs / (best * 1e-6) / 1e12, 1)}
+
+    out = {"topk": [], "pool": [], "history": []}
+    for k in (9, 18, 37, 74):
+        log(f"sweep topk {k}")
+        out["topk"].append(fwd_time(74, 32, k, 5000 + k))
+    for c in (0, 16, 32, 64):
+        log(f"sweep pool {c}")
+        out["pool"].append(fwd_time(74, c, 16, 5100 + c))
+    for h in (1, 2, 4, 8, 16, 27):
+        log(f"sweep history {h}")
+        dense = fwd_time(qb * h, 0, qb * h, 5200 + h)
+        w = qb * min(h, 2)
+        sparse = fwd_time(w, min(64, qb * max(0, h - 2)), min(16, w), 5300 + h)
+        out["history"].append({"chunks": h, "dense": dense, "pbsa": sparse,
+                               "speedup": round(dense["fwd_us"] / sparse["fwd_us"], 2)})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -256,6 +319,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--no-rollout", action="store_true", help="skip the 20 s / 1 min rollouts")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only the sparsity x history sweep of the forward (its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: PBSA shards by head with no exchange, and this build "
@@ -267,6 +332,9 @@ def main():
     from block_sparse_attention_20_amd.rollout import attended_tokens
     pkg.lib()
     dev = "cuda"
+    if args.sweep:
+        print(json.dumps({"sweep": sweep(torch, dev)}), flush=True)
+        return
     log(f"building 30-layer state ({args.layers} layers)")
     ro = build_rollout(args.layers, dev)
     torch.cuda.synchronize()

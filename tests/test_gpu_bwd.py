@@ -70,6 +70,10 @@ CASES = {
     # the per-(query block, slot) count table and takes the streaming scan
     "many_slots": (syn.Shape(B=1, H=1, d=64, T=64, Nq=100 * 64 - 10, W=128, C=2, topk=4),
                    dict(sigma=1.0, shift=1.0, n_planted=4, pool_count=2)),
+    # block lists longer than the 128 entries staged in LDS
+    "long_list": (syn.Shape(B=1, H=1, d=64, T=64, Nq=3 * 64 - 5, W=150, C=10, topk=140),
+                  dict(sigma=1.0, shift=1.0, n_planted=4, win_len=[64] * 70 + [0, 23] + [64] * 78,
+                       pool_count=10)),
 }
 
 

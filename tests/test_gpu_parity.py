@@ -113,6 +113,12 @@ CASES = {
     # W = 0, C = 0: the current chunk only
     "current_only": (syn.Shape(B=1, H=3, d=64, T=64, Nq=130, W=0, C=0, topk=0),
                      dict(sigma=1.0, win_len=[], pool_count=0)),
+    # a block list longer than the 128 entries staged in LDS (pool 12 + 140
+    # selected + 3 current): the entries past it are resolved on the fly
+    "long_list": (syn.Shape(B=1, H=2, d=128, T=64, Nq=3 * 64 - 5, W=150, C=12, topk=140),
+                  dict(sigma=1.0, shift=1.0, n_planted=4,
+                       win_len=[64] * 40 + [0, 30] + [64] * 100 + [17] + [64] * 7,
+                       pool_count=[12, 7])),
 }
 
 
