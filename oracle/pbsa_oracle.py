@@ -48,6 +48,10 @@ each reading is tagged R<n> and listed with its basis in the design notes:
   R15 placement: survivors keep their slots; freed slots, then the unused
       tail, are filled in ascending order by the admitted blocks in
       ascending id order; valid pool slots are always [0, count)
+  R16 fine-grained block mass (an alternative to R11's coarse mass): the
+      exact attention probability the chunk's query rows put on the block's
+      tokens, summed over the rows; a block a row does not attend gets
+      nothing from it
 """
 from __future__ import annotations
 
@@ -282,6 +286,46 @@ def attn_fwd(st: dict, sel: np.ndarray, sel_count: np.ndarray, scale: float, t: 
         o[b, h, rows.start:rows.stop] = (e / l) @ V
         lse[b, h, rows.start:rows.stop] = (m + np.log(l))[:, 0]
     return dict(o=o, lse=lse)
+
+
+def fine_mass(st: dict, sel: np.ndarray, sel_count: np.ndarray, scale: float, t: int) -> dict:
+    """Fine-grained block mass (R16): for every stored block j,
+    M_j = sum over the chunk's query rows r of sum_{u in j} P_ru, where P_r is
+    row r's attention distribution over its attended set U_i (the same one
+    attn_fwd normalises over).  Returns mass_pool [B,H,C], mass_win [B,H,W]
+    and, for the identity sum_j M_j = number of query rows, mass_cur
+    [B,H,QB] (current-chunk block c holds tokens [c t, c t + t))."""
+    st = as_f64_state(st)
+    q = st["q"]
+    B, H, nq, d = q.shape
+    qb = n_blocks(nq, t)
+    C = st["k_pool"].shape[2]
+    W = st["k_win"].shape[2]
+    mass_pool = np.zeros((B, H, C))
+    mass_win = np.zeros((B, H, W))
+    mass_cur = np.zeros((B, H, qb))
+    sel = np.asarray(sel); sel_count = np.asarray(sel_count)
+    for b in range(B):
+        for h in range(H):
+            for i in range(qb):
+                rows = query_block_rows(nq, t, i)
+                seg, K, _ = _block_operands(st, b, h, sel[b, h, i, :int(sel_count[b, h, i])])
+                z = scale * (q[b, h, rows.start:rows.stop] @ K.T)
+                e = np.exp(z - z.max(axis=1, keepdims=True))
+                P = e / e.sum(axis=1, keepdims=True)  # each row sums to 1
+                col_mass = P.sum(axis=0)             # per attended token
+                u0 = 0
+                for reg, slot, n in seg:
+                    m = col_mass[u0:u0 + n]
+                    if reg == "pool":
+                        mass_pool[b, h, slot] += m.sum()
+                    elif reg == "win":
+                        mass_win[b, h, slot] += m.sum()
+                    else:
+                        for c in range(qb):
+                            mass_cur[b, h, c] += m[c * t:min(n, (c + 1) * t)].sum()
+                    u0 += n
+    return dict(mass_pool=mass_pool, mass_win=mass_win, mass_cur=mass_cur)
 
 
 def attn_bwd(st: dict, sel: np.ndarray, sel_count: np.ndarray, dout: np.ndarray, scale: float,

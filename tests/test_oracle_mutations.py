@@ -43,6 +43,14 @@ MUTATIONS = [
     ("select", "pi = softmax(np.array(sp + [sw[w] for w in valid_w] + sc))",
      "pi = softmax(np.array(sp + [sw[w] for w in valid_w]))",
      ["test_mass_two_candidates_logistic", "test_mass_uniform_when_scores_equal"]),
+    ("fine_mass", "P = e / e.sum(axis=1, keepdims=True)", "P = e",
+     ["test_fine_mass_rows_sum_to_one", "test_fine_mass_uniform_when_queries_are_zero"]),
+    ("fine_mass", "mass_win[b, h, slot] += m.sum()", "mass_win[b, h, min(slot + 1, W - 1)] += m.sum()",
+     ["test_fine_mass_uniform_when_queries_are_zero", ("test_fine_mass_matches_bruteforce_token_mask", dict(T=4, d=8))]),
+    ("fine_mass", "col_mass = P.sum(axis=0)", "col_mass = P.sum(axis=0) * 0 + P[0]",
+     ["test_fine_mass_rows_sum_to_one"]),
+    ("fine_mass", "z = scale * (q[b, h, rows.start:rows.stop] @ K.T)", "z = (q[b, h, rows.start:rows.stop] @ K.T)",
+     [("test_fine_mass_matches_bruteforce_token_mask", dict(T=4, d=8))]),
     ("memory_update_one", "free = sorted(free)", "free = sorted(free, reverse=True)",
      ["test_update_placement_golden"]),
     ("memory_update_one", "admitted = sorted([x for x in kept if x[0] == \"cand\"], key=lambda x: x[2])",

@@ -358,6 +358,78 @@ def test_mass_sums_to_query_blocks_when_current_is_negligible():
     assert abs(total - 3.0) < 1e-12
 
 
+# ---------------------------------------------- fine-grained block mass ---
+def test_fine_mass_uniform_when_queries_are_zero():
+    # Q == 0 => every row attends its set U_i uniformly => a block j in U_i
+    # receives rows_i * len_j / |U_i| from query block i
+    T, nq = 4, 10
+    lens = [4, 4, 0, 1, 4, 3]
+    shape, st = small_state(H=2, d=8, T=T, Nq=nq, W=6, C=3, win_len=lens,
+                            pool_count=[2, 3], pool_len=[4, 2, 4, 4, 1, 3])
+    st["q"][:] = 0
+    sel = np.array([[[[0, 3, -1], [1, 4, 5], [5, -1, -1]],
+                     [[2, 4, -1], [0, 1, 3], [3, 4, -1]]]])
+    cnt = np.array([[[2, 3, 1], [2, 3, 2]]])
+    r = po.fine_mass(st, sel, cnt, 0.7, T)
+    for h in range(2):
+        n_pool = int(st["pool_count"][0, h])
+        plen = [int(x) for x in st["pool_len"][0, h]]
+        ep = np.zeros(3); ew = np.zeros(6); ec = np.zeros(3)
+        for i in range(3):
+            rows = min(T, nq - i * T)
+            chosen = [w for w in sel[0, h, i, :cnt[0, h, i]]]
+            n_u = sum(plen[:n_pool]) + sum(lens[w] for w in chosen) + nq
+            for p_ in range(n_pool):
+                ep[p_] += rows * plen[p_] / n_u
+            for w in chosen:
+                ew[w] += rows * lens[w] / n_u
+            for c in range(3):
+                ec[c] += rows * min(T, nq - c * T) / n_u
+        np.testing.assert_allclose(r["mass_pool"][0, h], ep, rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(r["mass_win"][0, h], ew, rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(r["mass_cur"][0, h], ec, rtol=1e-13, atol=1e-15)
+
+
+def test_fine_mass_rows_sum_to_one():
+    # every valid query row distributes exactly one unit of mass
+    shape, st = small_state(H=2, d=8, T=4, Nq=11, W=5, C=2, win_len=[4, 3, 4, 0, 4],
+                            pool_count=[2, 1], pool_len=[4, 2, 4, 4], seed=6)
+    r = po.select(st, 2, 0.5, 4)
+    f = po.fine_mass(st, r["sel"], r["sel_count"], 0.5, 4)
+    total = f["mass_pool"].sum(-1) + f["mass_win"].sum(-1) + f["mass_cur"].sum(-1)
+    np.testing.assert_allclose(total, 11.0, rtol=1e-13)
+    assert (f["mass_pool"] >= 0).all() and (f["mass_win"] >= 0).all()
+
+
+@pytest.mark.parametrize("T,d", [(2, 4), (4, 8)])
+def test_fine_mass_matches_bruteforce_token_mask(T, d):
+    # flat token axis [pool C*T | window W*T | current Nq], masked softmax by
+    # torch's library routine, then summed over each block's token range
+    C, W, nq = 3, 5, 3 * T + 1
+    shape, st = small_state(H=2, d=d, T=T, Nq=nq, W=W, C=C,
+                            win_len=[T, 1, 0, T, T - 1], pool_count=[3, 1],
+                            pool_len=[T, 1, T, T, T, T], seed=8)
+    scale = 0.8
+    r = po.select(st, 2, scale, T)
+    sel, cnt = r["sel"], r["sel_count"]
+    f = po.fine_mass(st, sel, cnt, scale, T)
+    mask, K, _ = _flat_token_mask(st, sel, cnt, T, C, W)
+    z = scale * torch.einsum("bhrd,bhud->bhru", st["q"].double(), K)
+    z = z.masked_fill(~torch.from_numpy(mask), float("-inf"))
+    P = torch.softmax(z, dim=-1).numpy()
+    col = P.sum(axis=2)                                    # [B,H,n_tok]
+    for h in range(2):
+        np.testing.assert_allclose(f["mass_pool"][0, h], col[0, h, :C * T].reshape(C, T).sum(-1),
+                                   rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(f["mass_win"][0, h],
+                                   col[0, h, C * T:C * T + W * T].reshape(W, T).sum(-1),
+                                   rtol=1e-12, atol=1e-14)
+        cur = col[0, h, C * T + W * T:]
+        np.testing.assert_allclose(f["mass_cur"][0, h],
+                                   [cur[c * T:(c + 1) * T].sum() for c in range(4)],
+                                   rtol=1e-12, atol=1e-14)
+
+
 # ----------------------------------------------------------- memory update ---
 def test_update_matches_best_subset_bruteforce():
     rng = np.random.default_rng(0)
