@@ -309,6 +309,108 @@ def sweep(torch, device="cuda", reps=3, iters=10):
     return out
 
 
+def mass_compare(torch, n_chunks=16, n_layers=2, device="cuda"):
+    """Coarse vs exact (fine-grained) block mass as the Top-C score, on the
+    streaming Wan-shaped rollout (pool cap 64, k = 16, 8 planted salient
+    blocks per chunk): per chunk, the overlap of the two pools (Jaccard over
+    (layer, head)); and for layer 0, with dense attention over the whole
+    history (the same kernel with every history block selected) and its
+    exact block masses, the share of the dense attention mass on blocks
+    older than the window that each pool holds, next to the best 64 blocks
+    chosen with hindsight.  Also the time of pbsa_fine_mass."""
+    import pbsa_synth as syn
+    from block_sparse_attention_20_amd.layer import PBSALayer
+    from block_sparse_attention_20_amd.rollout import Rollout
+    s = syn.WAN_CHUNK
+    C = syn.ROLLOUT_POOL_CAP
+    qb = s.QB
+    shape = syn.Shape(B=s.B, H=s.H, d=s.d, T=s.T, Nq=s.Nq, W=0, C=C, topk=s.topk)
+    ros = {m: Rollout(n_layers, s.B, s.H, s.d, s.T, s.Nq, C, s.topk, window_chunks=2, device=device,
+                      overlap=True, mass=m) for m in ("coarse", "fine")}
+    sigma = 1 / math.sqrt(s.d)
+    hist = []  # layer 0's chunks: (k, v) padded to whole blocks, [B,H,QB,T,d]
+    pad = qb * s.T - s.Nq
+
+    def blocks(x):
+        x = torch.nn.functional.pad(x, (0, 0, 0, pad))
+        return x.reshape(s.B, s.H, qb, s.T, s.d)
+
+    rows = []
+    for t in range(n_chunks):
+        for l in range(n_layers):
+            u = syn.rollout_direction(4, l, t, s.d, device=device)
+            ch = syn.make_chunk(shape, syn.rollout_seed(4, l, t), u, sigma=sigma, shift=1.5,
+                                n_planted=8, device=device)
+            for ro in ros.values():
+                ro.set_inputs(l, ch["q"], ch["k"], ch["v"])
+            if l == 0:
+                cur = ch
+        # layer 0's pool as this chunk attends it (before this chunk's update)
+        pools = {m: (ro.layers[0].t["pool_id"].clone(), ro.layers[0].t["pool_count"].clone())
+                 for m, ro in ros.items()}
+        ms = {}
+        for m, ro in ros.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for l in range(n_layers):
+                ro.run_layer(l)
+            e1.record()
+            ro.sync_side()
+            torch.cuda.synchronize()
+            ms[m] = e0.elapsed_time(e1)
+        row = {"chunk": t, "ms_coarse": round(ms["coarse"], 3), "ms_fine": round(ms["fine"], 3)}
+        # pool overlap after this chunk's update
+        jac = []
+        for l in range(n_layers):
+            pa = ros["coarse"].layers[l].t; pb = ros["fine"].layers[l].t
+            for h in range(s.H):
+                a = set(pa["pool_id"][0, h, :int(pa["pool_count"][0, h])].tolist())
+                b = set(pb["pool_id"][0, h, :int(pb["pool_count"][0, h])].tolist())
+                jac.append(len(a & b) / len(a | b) if a | b else 1.0)
+        row["pool_jaccard"] = round(sum(jac) / len(jac), 4)
+        if t >= 3:
+            # dense attention over every history chunk, layer 0
+            W = qb * t
+            D = PBSALayer(s.B, s.H, s.d, s.T, s.Nq, W, 0, W, device=device, ws_fwd=None)
+            D.t["q"].copy_(cur["q"]); D.t["k_cur"].copy_(cur["k"]); D.t["v_cur"].copy_(cur["v"])
+            D.t["k_win"].copy_(torch.cat([k for k, _ in hist], dim=2))
+            D.t["v_win"].copy_(torch.cat([v for _, v in hist], dim=2))
+            D.t["win_len"].copy_(torch.tensor(syn.chunk_window_lens(s.Nq, s.T, t), dtype=torch.int32))
+            D.t["win_id"].copy_(torch.arange(W, dtype=torch.int64))
+            D.refresh_kbar()
+            D.select(); D.fwd(); D.fine_mass()
+            md = D.t["mass_win"][0].double()            # [H, W]: block id = slot
+            old = (t - 2) * qb                           # ids older than the window
+            cap = {m: [] for m in ros}
+            best = []
+            for h in range(s.H):
+                tot = float(md[h, :old].sum())
+                best.append(float(md[h, :old].topk(min(C, old)).values.sum()) / tot)
+                for m in ros:
+                    pid, pcnt = pools[m]
+                    ids = pid[0, h, :int(pcnt[0, h])].long()
+                    cap[m].append(float(md[h, ids[ids < old]].sum()) / tot)
+            for m in ros:
+                row["pool_share_" + m] = round(sum(cap[m]) / s.H, 4)
+            row["pool_share_best"] = round(sum(best) / s.H, 4)
+            del D
+        hist.append((blocks(cur["k"]).clone(), blocks(cur["v"]).clone()))
+        rows.append(row)
+        for ro in ros.values():
+            ro.advance()
+    # pbsa_fine_mass alone on layer 0 of the fine rollout (last chunk's state)
+    L = ros["fine"].layers[0]
+    L.fine_mass(); torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        L.fine_mass()
+    e1.record(); torch.cuda.synchronize()
+    return {"workload": f"streaming rollout, {n_chunks} chunks x {n_layers} layers, pool cap {C}, "
+                        "coarse vs exact block mass as the Top-C score",
+            "per_chunk": rows, "fine_mass_us": round(e0.elapsed_time(e1) * 1e3 / 20, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,6 +423,8 @@ def main():
     ap.add_argument("--no-rollout", action="store_true", help="skip the 20 s / 1 min rollouts")
     ap.add_argument("--sweep", action="store_true",
                     help="only the sparsity x history sweep of the forward (its own JSON line)")
+    ap.add_argument("--mass-compare", action="store_true",
+                    help="only the coarse vs exact block-mass comparison (its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: PBSA shards by head with no exchange, and this build "
@@ -334,6 +438,9 @@ def main():
     dev = "cuda"
     if args.sweep:
         print(json.dumps({"sweep": sweep(torch, dev)}), flush=True)
+        return
+    if args.mass_compare:
+        print(json.dumps({"mass_compare": mass_compare(torch, device=dev)}), flush=True)
         return
     log(f"building 30-layer state ({args.layers} layers)")
     ro = build_rollout(args.layers, dev)

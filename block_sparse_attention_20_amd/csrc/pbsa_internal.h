@@ -16,6 +16,7 @@ size_t select_lds_bytes(const pbsa_problem &p);
 size_t update_ws_bytes(const pbsa_problem &p);
 size_t fwd_ws_bytes(const pbsa_problem &p);
 size_t bwd_ws_bytes(const pbsa_problem &p);
+size_t fine_ws_bytes(const pbsa_problem &p);
 
 hipError_t launch_select(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
                          int32_t *sel, int32_t *sel_count, float *mass_pool, float *mass_win,
@@ -34,6 +35,9 @@ hipError_t launch_attn_bwd(const pbsa_problem &p, float scale, const void *q, co
                            const int32_t *sel, const int32_t *sel_count, const void *o,
                            const float *lse, const void *dout, void *dq, const pbsa_kv_grad &g,
                            void *ws, hipStream_t st);
+hipError_t launch_fine_mass(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
+                            const int32_t *sel, const int32_t *sel_count, const float *lse,
+                            float *mass_pool, float *mass_win, void *ws, hipStream_t st);
 hipError_t launch_memory_update(const pbsa_problem &p, const pbsa_kv &kv, const float *mass_pool,
                                 const float *mass_win, const int32_t *leaving, int n_leave,
                                 int64_t n_sink, void *ws, hipStream_t st);

@@ -57,6 +57,7 @@ class PBSALayer:
         # runs one workgroup per query block, a tensor is shared (layers that
         # run one after another on one stream can share it)
         self.ws_fwd = P.workspace(self.prob, P.PBSA_OP_FWD, device) if isinstance(ws_fwd, str) else ws_fwd
+        self.ws_fine = None  # allocated on first use of fine_mass()
         self._kv = None
 
     # -- state ---------------------------------------------------------------
@@ -98,6 +99,17 @@ class PBSALayer:
         t = self.t
         P.pbsa_block_mass(self.prob, t["mass_pool"] if self.C > 0 else None,
                           t["mass_win"] if self.W > 0 else None, self.ws_select)
+
+    def fine_mass(self, stream=None):
+        """Exact block masses from the last fwd's lse (pbsa_fine_mass) into
+        mass_pool / mass_win, in place of the coarse ones; the update reads
+        whichever was written last."""
+        t = self.t
+        if self.ws_fine is None:
+            self.ws_fine = P.workspace(self.prob, P.PBSA_OP_FINE_MASS, self.device)
+        P.pbsa_fine_mass(self.prob, t["q"], self.kv, t["sel"] if self.topk > 0 else None,
+                         t["sel_count"], t["lse"], t["mass_pool"] if self.C > 0 else None,
+                         t["mass_win"] if self.W > 0 else None, self.ws_fine, stream)
 
     def fwd(self, with_lse=True):
         t = self.t

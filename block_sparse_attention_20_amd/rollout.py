@@ -19,6 +19,9 @@ Per layer and chunk t (all device work is libpbsa.so; nothing syncs):
 The state of a layer is plain device tensors (``PBSALayer.t``), so it can be
 saved and restored with ``state_dict`` / ``load_state_dict``.
 
+With ``mass="fine"`` the update ranks blocks by their exact attention mass
+(pbsa_fine_mass, from the forward's lse) instead of the coarse mass.
+
 With ``overlap=True`` steps 2-3 go to a side stream: the next layer needs
 only this layer's output O, while the masses and the updated pool and window
 are needed by the next *chunk*.  The side stream waits for the layer's
@@ -42,7 +45,10 @@ STATE_KEYS = ("k_win", "v_win", "win_len", "win_id", "kbar_win", "k_pool", "v_po
 class Rollout:
     def __init__(self, n_layers: int, B: int, H: int, d: int, T: int, Nq: int, C: int, topk: int,
                  n_sink: int = 0, window_chunks: int = 2, dtype=torch.bfloat16, scale: float = 0.0,
-                 device="cuda", overlap: bool = False):
+                 device="cuda", overlap: bool = False, mass: str = "coarse"):
+        if mass not in ("coarse", "fine"):
+            raise ValueError(f"mass must be 'coarse' or 'fine', not {mass!r}")
+        self.mass = mass
         self.QB = (Nq + T - 1) // T
         self.window_chunks = window_chunks
         self.W = window_chunks * self.QB
@@ -85,7 +91,8 @@ class Rollout:
         self._wait_side(layer)
         # with a side stream the block masses (needed only by the update) are
         # computed there, off the attention's critical path
-        L.select(masses=self.side is None)
+        L.select(masses=self.side is None and self.mass == "coarse")
+        self._attended = attention
         if attention:
             if fwd_events is not None:
                 fwd_events[0].record()
@@ -104,8 +111,10 @@ class Rollout:
 
     def _side_work(self, L, t):
         if t >= self.window_chunks:
-            if self.side is not None:
-                L.block_mass()
+            if self.mass == "fine" and self._attended:
+                L.fine_mass()        # reads this chunk's lse
+            elif self.side is not None or self.mass == "fine":
+                L.block_mass()       # coarse masses from the select scores
             L.update(self.leaving[t % self.window_chunks], self.n_sink)
         L.append_window(self.first_slot(t), t * self.QB)
 

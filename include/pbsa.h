@@ -74,7 +74,8 @@ enum {
   PBSA_ERR_UNSUPPORTED = -7  /* valid but not implemented (e.g. d = 96) */
 };
 
-enum { PBSA_OP_SELECT = 0, PBSA_OP_FWD = 1, PBSA_OP_BWD = 2, PBSA_OP_UPDATE = 3 };
+enum { PBSA_OP_SELECT = 0, PBSA_OP_FWD = 1, PBSA_OP_BWD = 2, PBSA_OP_UPDATE = 3,
+       PBSA_OP_FINE_MASS = 4 };
 
 /* Bits OR-ed into *dev_status by kernels (device-side metadata faults). */
 enum {
@@ -188,6 +189,27 @@ int pbsa_attn_bwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const
                   const int32_t *sel_count, const void *o, const float *lse, const void *dout,
                   void *dq, const pbsa_kv_grad *g, void *ws, size_t ws_bytes,
                   pbsa_stream_t stream);
+
+/*
+ * pbsa_fine_mass - exact block mass, an alternative score for the Top-C
+ * update ("Arquitectura Propuesta": dynamic pool blocks are kept by their
+ * relevance to the current step; this scores that relevance with the
+ * attention itself instead of pooled representatives).  For every stored
+ * block j of (b, h):
+ *   M_j = sum over the chunk's query rows r of sum_{u in j} P_ru,
+ *   P_ru = exp(scale <Q_r, K_u> - lse_r),
+ * with lse the natural-log output of pbsa_attn_fwd for the same problem,
+ * q, kv, sel and sel_count, so that P is the forward's attention.  mass_pool
+ * [B,H,C] covers pool slots [0, count) (0 elsewhere); mass_win [B,H,W] sums
+ * over the query blocks that selected the slot (0 if none did).  Both are
+ * required (when C > 0 / W > 0), fp32, written in full, and can be passed
+ * to pbsa_memory_update in place of the coarse masses.
+ * Workspace: pbsa_workspace_size(p, PBSA_OP_FINE_MASS) bytes (partial sums;
+ * no initialisation needed).
+ */
+int pbsa_fine_mass(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const int32_t *sel,
+                   const int32_t *sel_count, const float *lse, float *mass_pool, float *mass_win,
+                   void *ws, size_t ws_bytes, pbsa_stream_t stream);
 
 /*
  * pbsa_memory_update - Top-C retention of the persistent pool ("Arquitectura

@@ -48,7 +48,7 @@ each reading is tagged R<n> and listed with its basis in the design notes:
   R15 placement: survivors keep their slots; freed slots, then the unused
       tail, are filled in ascending order by the admitted blocks in
       ascending id order; valid pool slots are always [0, count)
-  R16 fine-grained block mass (an alternative to R11's coarse mass): the
+  R19 fine-grained block mass (an alternative to R11's coarse mass): the
       exact attention probability the chunk's query rows put on the block's
       tokens, summed over the rows; a block a row does not attend gets
       nothing from it
@@ -289,7 +289,7 @@ def attn_fwd(st: dict, sel: np.ndarray, sel_count: np.ndarray, scale: float, t: 
 
 
 def fine_mass(st: dict, sel: np.ndarray, sel_count: np.ndarray, scale: float, t: int) -> dict:
-    """Fine-grained block mass (R16): for every stored block j,
+    """Fine-grained block mass (R19): for every stored block j,
     M_j = sum over the chunk's query rows r of sum_{u in j} P_ru, where P_r is
     row r's attention distribution over its attended set U_i (the same one
     attn_fwd normalises over).  Returns mass_pool [B,H,C], mass_win [B,H,W]

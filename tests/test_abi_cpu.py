@@ -76,6 +76,10 @@ def test_workspace_sizes():
     assert P.pbsa_workspace_size(p, P.PBSA_OP_UPDATE) >= 2 * 12 * 32 * 4 + 12 * 4
     bad = wan(); bad.d = 96
     assert P.pbsa_workspace_size(bad, P.PBSA_OP_SELECT) == 0
+    # fine mass: one fp32 partial sum per (b, h, query block, wave slot, entry)
+    assert P.pbsa_workspace_size(p, P.PBSA_OP_FINE_MASS) >= 12 * 37 * 4 * (32 + 16) * 4
+    assert P.pbsa_validate(p, P.PBSA_OP_FINE_MASS) == 0
+    assert P.pbsa_validate(p, P.PBSA_OP_FINE_MASS + 1) == -2
 
 
 def test_entry_points_reject_before_launch():
@@ -115,4 +119,12 @@ def test_entry_points_reject_before_launch():
     g = P.KVGrad()
     assert L.pbsa_attn_bwd(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, fake, fake, fake,
                            ctypes.byref(g), fake, 1 << 30, None) == -1
+    # fine mass: lse and both mass buffers required, workspace sized
+    need = L.pbsa_workspace_size(ctypes.byref(p), P.PBSA_OP_FINE_MASS)
+    assert L.pbsa_fine_mass(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, None, fake, fake, fake,
+                            need, None) == -1
+    assert L.pbsa_fine_mass(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, None, fake, fake,
+                            need, None) == -1
+    assert L.pbsa_fine_mass(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, fake, fake, fake,
+                            need - 1, None) == -5
     assert L.pbsa_strerror(-5).decode().startswith("workspace")

@@ -155,6 +155,41 @@ def test_select_and_fwd_match_oracle(name):
     assert L.status_bits() == 0
 
 
+@pytest.mark.parametrize("name", ["bf16_d128_T128_small", "bf16_d64_T64_multi", "bf16_d64_T128",
+                                  "bf16_d128_T64", "f32_d64_T64", "f32_d128_T128",
+                                  "empty_pool_and_window", "topk_covers_window", "long_list"])
+def test_fine_mass_matches_oracle(name):
+    """Exact block masses from the forward's lse against the fp64 oracle on
+    the GPU's own selection.  Bar: 5e-3 of the largest mass (bf16 rounding is
+    shared, so the residue is the fp32 accumulation and the forward's lse
+    error, <= 2e-3 in these cases), 5e-5 for fp32; blocks no row attends are
+    exact zeros."""
+    shape, kw = CASES[name]
+    _log(f"fine mass case {name}")
+    st = syn.make_state(shape, 13, pad_value=float("nan"), **kw)
+    L = run(shape, st)
+    # poison the mass buffers: every element must be written
+    L.t["mass_pool"].fill_(float("nan")); L.t["mass_win"].fill_(float("nan"))
+    L.fine_mass()
+    torch.cuda.synchronize()
+    scale = eff_scale(shape, 0.0)
+    gsel = L.t["sel"].cpu().numpy(); gcnt = L.t["sel_count"].cpu().numpy()
+    ref = po.fine_mass(st, gsel, gcnt, scale, shape.T)
+    rtol = 5e-5 if shape.dtype == torch.float32 else 5e-3
+    for n, C in (("mass_pool", shape.C), ("mass_win", shape.W)):
+        if C == 0:
+            continue
+        got = L.t[n].cpu().numpy()[..., :C]
+        r = ref[n]
+        assert not np.isnan(got).any(), f"{name}: {n} not fully written"
+        bar = rtol * max(np.abs(r).max(), 1e-30) + 1e-7
+        err = np.abs(got - r).max()
+        _log(f"{name} {n}: max-abs {err:.3e} (bar {bar:.3e})")
+        assert err <= bar, (name, n, err, bar)
+        assert (got[r == 0] == 0).all(), f"{name}: {n} nonzero where no row attends"
+    assert L.status_bits() == 0
+
+
 @pytest.mark.parametrize("name", ["bf16_d128_T128_small", "bf16_d64_T64_multi", "bf16_d128_T64",
                                   "empty_pool_and_window"])
 def test_fwd_split_and_one_block_per_workgroup_agree(name):
@@ -321,3 +356,48 @@ def test_wan_chunk_full_size(unscaled):
     lref = np.concatenate([f["lse"][0, h, rows] for h in (0, 5, 11)])
     lgot = np.concatenate([lse[0, h, rows] for h in (0, 5, 11)])
     assert np.abs(lgot - lref).max() <= 2e-3
+
+
+def _one_head(st, h):
+    """State of head h alone (B = 1): per-head tensors sliced, shared ones kept."""
+    out = {}
+    for k, v in st.items():
+        if k in ("win_len", "win_id", "planted", "u"):
+            out[k] = v
+        elif hasattr(v, "dim") and v.dim() >= 2:
+            out[k] = v[:, h:h + 1]
+        else:
+            out[k] = v
+    return out
+
+
+@pytest.mark.parametrize("unscaled", [False, True])
+def test_fine_mass_wan_chunk_full_size(unscaled):
+    """Exact block masses at the Wan chunk, full size: two heads against the
+    oracle (all their query blocks), every head checked for the identity
+    sum of pool + window masses <= query rows, and the planted window
+    blocks (chosen by every query block) holding more mass than the rest."""
+    _log(f"fine mass wan chunk unscaled={unscaled}")
+    shape = syn.WAN_CHUNK
+    st = syn.wan_chunk_state(0, unscaled=unscaled)
+    L = run(shape, st)
+    L.t["mass_pool"].fill_(float("nan")); L.t["mass_win"].fill_(float("nan"))
+    L.fine_mass()
+    torch.cuda.synchronize()
+    mp = L.t["mass_pool"].cpu().numpy(); mw = L.t["mass_win"].cpu().numpy()
+    assert not np.isnan(mp).any() and not np.isnan(mw).any()
+    tot = mp.sum(-1) + mw.sum(-1)
+    assert (tot > 0).all() and (tot <= shape.Nq * (1 + 1e-3)).all()
+    gsel = L.t["sel"].cpu().numpy(); gcnt = L.t["sel_count"].cpu().numpy()
+    scale = 1 / math.sqrt(128)
+    for h in (0, 7):
+        ref = po.fine_mass(_one_head(st, h), gsel[:, h:h + 1], gcnt[:, h:h + 1], scale, shape.T)
+        for n, got in (("mass_pool", mp[:, h:h + 1]), ("mass_win", mw[:, h:h + 1])):
+            r = ref[n]
+            err = np.abs(got - r).max()
+            bar = 5e-3 * np.abs(r).max() + 1e-7
+            _log(f"head {h} {n}: max-abs {err:.3e} (bar {bar:.3e}), max {np.abs(r).max():.3e}")
+            assert err <= bar, (h, n, err, bar)
+    planted = st["planted"]
+    others = [w for w in range(shape.W) if w not in planted]
+    assert mw[0][:, planted].min() > mw[0][:, others].max()
