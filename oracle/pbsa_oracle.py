@@ -48,6 +48,8 @@ each reading is tagged R<n> and listed with its basis in the design notes:
   R15 placement: survivors keep their slots; freed slots, then the unused
       tail, are filled in ascending order by the admitted blocks in
       ascending id order; valid pool slots are always [0, count)
+  R20 head-shared pool (a policy variant): every head of a batch element
+      ranks the candidates by the block's masses summed over the heads
   R19 fine-grained block mass (an alternative to R11's coarse mass): the
       exact attention probability the chunk's query rows put on the block's
       tokens, summed over the rows; a block a row does not attend gets
@@ -429,14 +431,46 @@ def memory_update_one(pool_ids: list, pool_mass: list, cand_ids: list, cand_mass
     return assign, [new_ids[p] for p in range(count)], status
 
 
+def head_shared_masses(st: dict, mass_pool: np.ndarray, mass_win: np.ndarray):
+    """R20 (head-shared pool): the score of a block for batch element b is
+    the sum of its masses over the heads, matched by block id: per head, the
+    pool slot holding the id, or the window slot (shared by all heads).
+    Returns mass arrays of the input shapes holding those sums."""
+    st = as_f64_state(st)
+    pool_id = np.asarray(st["pool_id"]); pool_count = np.asarray(st["pool_count"])
+    win_id = np.asarray(st["win_id"])
+    B, H, C = pool_id.shape
+    W = win_id.shape[0]
+    mp = np.zeros((B, H, C)); mw = np.zeros((B, H, W))
+    for b in range(B):
+        tot = {}
+        for h in range(H):
+            for p in range(int(pool_count[b, h])):
+                x = int(pool_id[b, h, p])
+                tot[x] = tot.get(x, 0.0) + float(mass_pool[b, h, p])
+        for w in range(W):
+            x = int(win_id[w])
+            tot[x] = tot.get(x, 0.0) + float(sum(mass_win[b, h, w] for h in range(H)))
+        for h in range(H):
+            for p in range(int(pool_count[b, h])):
+                mp[b, h, p] = tot[int(pool_id[b, h, p])]
+            for w in range(W):
+                mw[b, h, w] = tot[int(win_id[w])]
+    return mp, mw
+
+
 def memory_update(st: dict, mass_pool: np.ndarray, mass_win: np.ndarray, leaving: Iterable[int],
                   n_sink: int, kbar_win: Optional[np.ndarray] = None,
-                  kbar_pool: Optional[np.ndarray] = None) -> dict:
+                  kbar_pool: Optional[np.ndarray] = None, shared_heads: bool = False) -> dict:
     """Apply the Top-C update to every (b, h) and return the new pool state
     (copies; the inputs are not modified).  Leaving slots that are empty
     (len 0) are not candidates.  Pool K/V/len/id (and the pooled means if
     given) of admitted blocks are bit-exact copies of their window slot (R14).
+    With ``shared_heads`` every head ranks by the head-summed masses (R20),
+    so heads that hold the same pool make the same decision.
     """
+    if shared_heads:
+        mass_pool, mass_win = head_shared_masses(st, mass_pool, mass_win)
     st = as_f64_state(st)
     k_pool = np.array(st["k_pool"], copy=True); v_pool = np.array(st["v_pool"], copy=True)
     pool_len = np.array(st["pool_len"], copy=True); pool_id = np.array(st["pool_id"], copy=True)

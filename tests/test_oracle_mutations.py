@@ -51,6 +51,9 @@ MUTATIONS = [
      ["test_fine_mass_rows_sum_to_one"]),
     ("fine_mass", "z = scale * (q[b, h, rows.start:rows.stop] @ K.T)", "z = (q[b, h, rows.start:rows.stop] @ K.T)",
      [("test_fine_mass_matches_bruteforce_token_mask", dict(T=4, d=8))]),
+    ("head_shared_masses", "tot[x] = tot.get(x, 0.0) + float(mass_pool[b, h, p])",
+     "tot[x] = float(mass_pool[b, h, p])",
+     ["test_update_head_shared_pool_is_best_subset_of_summed_mass"]),
     ("memory_update_one", "free = sorted(free)", "free = sorted(free, reverse=True)",
      ["test_update_placement_golden"]),
     ("memory_update_one", "admitted = sorted([x for x in kept if x[0] == \"cand\"], key=lambda x: x[2])",

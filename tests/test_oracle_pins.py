@@ -459,6 +459,40 @@ def test_update_matches_best_subset_bruteforce():
         assert status == 0
 
 
+def test_update_head_shared_pool_is_best_subset_of_summed_mass():
+    # head-shared pool: heads hold the same blocks; the kept set must be the
+    # best C-subset by the mass summed over heads (brute force), and every
+    # head ends with the same pool
+    rng = np.random.default_rng(3)
+    C, H, W = 4, 3, 6
+    for trial in range(20):
+        shape, st = small_state(H=H, d=4, T=2, Nq=4, W=W, C=C, win_len=[2] * W,
+                                pool_count=4, pool_len=[2] * C, seed=trial)
+        st["pool_id"][:] = torch.tensor([3, 9, 14, 20])
+        st["win_id"][:] = torch.arange(30, 30 + W)
+        mp = rng.random((1, H, C)); mw = rng.random((1, H, W))
+        leaving = [1, 2, 4]
+        r = po.memory_update(st, mp, mw, leaving, 0, shared_heads=True)
+        ids = [3, 9, 14, 20] + [30 + w for w in leaving]
+        summed = dict(zip(ids, list(mp[0].sum(0)) + [mw[0, :, w].sum() for w in leaving]))
+        best = max(itertools.combinations(ids, C), key=lambda sub: sum(summed[i] for i in sub))
+        for h in range(H):
+            n = int(r["pool_count"][0, h])
+            assert set(r["pool_id"][0, h, :n].tolist()) == set(best), trial
+            np.testing.assert_array_equal(r["pool_id"][0, h], r["pool_id"][0, 0])
+
+
+def test_update_head_shared_pool_with_one_head_is_the_plain_update():
+    shape, st = small_state(H=1, d=4, T=2, Nq=4, W=5, C=3, win_len=[2, 2, 0, 2, 1],
+                            pool_count=3, pool_len=[2, 2, 2], seed=5)
+    rng = np.random.default_rng(1)
+    mp = rng.random((1, 1, 3)); mw = rng.random((1, 1, 5))
+    a = po.memory_update(st, mp, mw, [0, 1, 3, 4], 0)
+    b = po.memory_update(st, mp, mw, [0, 1, 3, 4], 0, shared_heads=True)
+    for k in ("pool_id", "pool_count", "pool_len", "k_pool"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
 def test_update_placement_golden():
     g = _read_golden("update_hand.txt")
     assign, new_ids, status = po.memory_update_one(
