@@ -310,7 +310,8 @@ def sweep(torch, device="cuda", reps=3, iters=10):
 
 
 def mass_compare(torch, n_chunks=16, n_layers=2, device="cuda"):
-    """Coarse vs exact (fine-grained) block mass as the Top-C score, on the
+    """Coarse vs exact (fine-grained) block mass as the Top-C score, and the
+    head-shared pool (one pool per layer, coarse masses summed over heads), on the
     streaming Wan-shaped rollout (pool cap 64, k = 16, 8 planted salient
     blocks per chunk): per chunk, the overlap of the two pools (Jaccard over
     (layer, head)); and for layer 0, with dense attention over the whole
@@ -327,6 +328,9 @@ def mass_compare(torch, n_chunks=16, n_layers=2, device="cuda"):
     shape = syn.Shape(B=s.B, H=s.H, d=s.d, T=s.T, Nq=s.Nq, W=0, C=C, topk=s.topk)
     ros = {m: Rollout(n_layers, s.B, s.H, s.d, s.T, s.Nq, C, s.topk, window_chunks=2, device=device,
                       overlap=True, mass=m) for m in ("coarse", "fine")}
+    # the head-shared pool variant: one pool per layer, coarse masses summed over heads
+    ros["shared"] = Rollout(n_layers, s.B, s.H, s.d, s.T, s.Nq, C, s.topk, window_chunks=2,
+                            device=device, overlap=True, shared_pool=True)
     sigma = 1 / math.sqrt(s.d)
     hist = []  # layer 0's chunks: (k, v) padded to whole blocks, [B,H,QB,T,d]
     pad = qb * s.T - s.Nq
@@ -358,7 +362,8 @@ def mass_compare(torch, n_chunks=16, n_layers=2, device="cuda"):
             ro.sync_side()
             torch.cuda.synchronize()
             ms[m] = e0.elapsed_time(e1)
-        row = {"chunk": t, "ms_coarse": round(ms["coarse"], 3), "ms_fine": round(ms["fine"], 3)}
+        row = {"chunk": t, "ms_coarse": round(ms["coarse"], 3), "ms_fine": round(ms["fine"], 3),
+               "ms_shared": round(ms["shared"], 3)}
         # pool overlap after this chunk's update
         jac = []
         for l in range(n_layers):
@@ -407,7 +412,7 @@ def mass_compare(torch, n_chunks=16, n_layers=2, device="cuda"):
         L.fine_mass()
     e1.record(); torch.cuda.synchronize()
     return {"workload": f"streaming rollout, {n_chunks} chunks x {n_layers} layers, pool cap {C}, "
-                        "coarse vs exact block mass as the Top-C score",
+                        "coarse vs exact block mass as the Top-C score, and a head-shared pool",
             "per_chunk": rows, "fine_mass_us": round(e0.elapsed_time(e1) * 1e3 / 20, 1)}
 
 

@@ -230,9 +230,10 @@ int pbsa_fine_mass(const pbsa_problem *p, const void *q, const pbsa_kv *kv, cons
                                            mass_win, ws, (hipStream_t)stream));
 }
 
-int pbsa_memory_update(const pbsa_problem *p, const pbsa_kv *kv, const float *mass_pool,
-                       const float *mass_win, const int32_t *leaving, int32_t n_leave,
-                       int64_t n_sink, void *ws, size_t ws_bytes, pbsa_stream_t stream) {
+static int memory_update_impl(const pbsa_problem *p, const pbsa_kv *kv, const float *mass_pool,
+                              const float *mass_win, const int32_t *leaving, int32_t n_leave,
+                              int64_t n_sink, void *ws, size_t ws_bytes, pbsa_stream_t stream,
+                              bool shared) {
   int rc = check_problem(p, PBSA_OP_UPDATE);
   if (rc) return rc;
   if ((rc = check_kv_common(kv, p))) return rc;
@@ -250,7 +251,21 @@ int pbsa_memory_update(const pbsa_problem *p, const pbsa_kv *kv, const float *ma
   }
   if ((rc = check_ws(p, PBSA_OP_UPDATE, ws, ws_bytes))) return rc;
   return hip_status(pbsa::launch_memory_update(*p, *kv, mass_pool, mass_win, leaving, n_leave,
-                                               n_sink, ws, (hipStream_t)stream));
+                                               n_sink, shared, ws, (hipStream_t)stream));
+}
+
+int pbsa_memory_update(const pbsa_problem *p, const pbsa_kv *kv, const float *mass_pool,
+                       const float *mass_win, const int32_t *leaving, int32_t n_leave,
+                       int64_t n_sink, void *ws, size_t ws_bytes, pbsa_stream_t stream) {
+  return memory_update_impl(p, kv, mass_pool, mass_win, leaving, n_leave, n_sink, ws, ws_bytes,
+                            stream, false);
+}
+
+int pbsa_memory_update_shared(const pbsa_problem *p, const pbsa_kv *kv, const float *mass_pool,
+                              const float *mass_win, const int32_t *leaving, int32_t n_leave,
+                              int64_t n_sink, void *ws, size_t ws_bytes, pbsa_stream_t stream) {
+  return memory_update_impl(p, kv, mass_pool, mass_win, leaving, n_leave, n_sink, ws, ws_bytes,
+                            stream, true);
 }
 
 int pbsa_block_mean(const pbsa_problem *p, const void *x, const int32_t *len, int64_t n_blocks,

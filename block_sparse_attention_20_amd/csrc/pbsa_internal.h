@@ -40,6 +40,6 @@ hipError_t launch_fine_mass(const pbsa_problem &p, float scale, const void *q, c
                             float *mass_pool, float *mass_win, void *ws, hipStream_t st);
 hipError_t launch_memory_update(const pbsa_problem &p, const pbsa_kv &kv, const float *mass_pool,
                                 const float *mass_win, const int32_t *leaving, int n_leave,
-                                int64_t n_sink, void *ws, hipStream_t st);
+                                int64_t n_sink, bool shared, void *ws, hipStream_t st);
 
 }  // namespace pbsa

@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void update_decide_kernel(
     const int64_t *__restrict__ win_id, int32_t *__restrict__ pool_len,
     int64_t *__restrict__ pool_id, int32_t *__restrict__ pool_count, int32_t *__restrict__ a_slot,
     int32_t *__restrict__ a_src, int32_t *__restrict__ a_count, int H, int W, int C, int T,
-    int64_t n_sink, int32_t *status) {
+    int64_t n_sink, int shared, int32_t *status) {
   __shared__ int64_t xid[kMaxX];
   __shared__ float xm[kMaxX];
   __shared__ int32_t xsrc[kMaxX];   // >= 0: pool slot; < 0: window slot -1-w
@@ -45,9 +45,18 @@ __global__ __launch_bounds__(256) void update_decide_kernel(
     if (t == 0) set_status(status, PBSA_STATUS_POOL_COUNT);
     n_pool = max(0, min(n_pool, C));
   }
+  // head-shared pool: every head of batch element b ranks by the masses
+  // summed over its heads (ascending h, so every head computes the same
+  // sums); the heads hold the same blocks in the same slots
+  const size_t b0 = (size_t)blockIdx.y * H;
   for (int p = t; p < n_pool; p += 256) {
     xid[p] = pool_id[bh * C + p];
-    xm[p] = mass_pool[bh * C + p];
+    float m = mass_pool[bh * C + p];
+    if (shared) {
+      m = 0.f;
+      for (int h2 = 0; h2 < H; ++h2) m += mass_pool[(b0 + h2) * C + p];
+    }
+    xm[p] = m;
     xsrc[p] = p;
   }
   // stage the leaving slots' metadata (wl = -1 marks a slot out of range)
@@ -78,7 +87,12 @@ __global__ __launch_bounds__(256) void update_decide_kernel(
     for (int c2 = 0; c2 < c; ++c2) pos += cflag[c2];
     const int w = lw[c];
     xid[pos] = lid[c];
-    xm[pos] = mass_win[bh * W + w];
+    float m = mass_win[bh * W + w];
+    if (shared) {
+      m = 0.f;
+      for (int h2 = 0; h2 < H; ++h2) m += mass_win[(b0 + h2) * W + w];
+    }
+    xm[pos] = m;
     xsrc[pos] = -1 - w;
   }
   int nc = 0, np = 0;
@@ -156,6 +170,23 @@ __global__ __launch_bounds__(256) void update_decide_kernel(
   if (t == 0) a_count[bh] = red[0] + red[1] + red[2] + red[3];
 }
 
+// Head-shared pool precondition, checked before the decisions (which then
+// rewrite the pool metadata): every head of batch element blockIdx.x holds
+// head 0's count and ids; otherwise PBSA_STATUS_SHARED.
+__global__ __launch_bounds__(256) void update_shared_check_kernel(const int64_t *__restrict__ pool_id,
+                                                                  const int32_t *__restrict__ pool_count,
+                                                                  int H, int C, int32_t *status) {
+  const size_t b0 = (size_t)blockIdx.x * H;
+  const int n0 = pool_count[b0];
+  bool bad = false;
+  for (int x = threadIdx.x; x < H * C; x += 256) {
+    const int h = x / C, p = x % C;
+    if (p == 0 && pool_count[b0 + h] != n0) bad = true;
+    if (p < n0 && p < C && pool_id[(b0 + h) * C + p] != pool_id[b0 * C + p]) bad = true;
+  }
+  if (bad) set_status(status, PBSA_STATUS_SHARED);
+}
+
 // grid (A, H, B): workgroup a copies admitted block a of (b, h) from its
 // window slot into its pool slot (K and V: all T rows; kbar: d floats).
 __global__ __launch_bounds__(256) void update_copy_kernel(
@@ -190,15 +221,18 @@ size_t update_ws_bytes(const pbsa_problem &p) {
 
 hipError_t launch_memory_update(const pbsa_problem &p, const pbsa_kv &kv, const float *mass_pool,
                                 const float *mass_win, const int32_t *leaving, int n_leave,
-                                int64_t n_sink, void *ws, hipStream_t st) {
+                                int64_t n_sink, bool shared, void *ws, hipStream_t st) {
   const size_t bh = (size_t)p.B * p.H;
   char *w = reinterpret_cast<char *>(ws);
   int32_t *a_slot = reinterpret_cast<int32_t *>(w);
   int32_t *a_src = reinterpret_cast<int32_t *>(w + align256(bh * p.C * sizeof(int32_t)));
   int32_t *a_count = reinterpret_cast<int32_t *>(w + 2 * align256(bh * p.C * sizeof(int32_t)));
+  if (shared && p.dev_status)
+    update_shared_check_kernel<<<p.B, 256, 0, st>>>(kv.pool_id, kv.pool_count, p.H, p.C, p.dev_status);
   update_decide_kernel<<<dim3(p.H, p.B), 256, 0, st>>>(
       mass_pool, mass_win, leaving, n_leave, kv.win_len, kv.win_id, kv.pool_len, kv.pool_id,
-      kv.pool_count, a_slot, a_src, a_count, p.H, p.W, p.C, p.T, n_sink, p.dev_status);
+      kv.pool_count, a_slot, a_src, a_count, p.H, p.W, p.C, p.T, n_sink, shared ? 1 : 0,
+      p.dev_status);
   const int A = n_leave < p.C ? n_leave : p.C;
   if (A > 0) {
     const size_t esz = p.dtype == PBSA_BF16 ? 2 : 4;

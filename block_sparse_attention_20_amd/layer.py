@@ -127,11 +127,13 @@ class PBSALayer:
                         self.ws_bwd)
         return grads
 
-    def update(self, leaving: torch.Tensor, n_sink: int = 0):
+    def update(self, leaving: torch.Tensor, n_sink: int = 0, shared: bool = False):
+        """Top-C update; shared=True ranks by the masses summed over heads
+        (pbsa_memory_update_shared: one pool for all heads)."""
         t = self.t
-        P.pbsa_memory_update(self.prob, self.kv, t["mass_pool"] if self.C > 0 else None,
-                             t["mass_win"] if self.W > 0 else None, leaving, leaving.numel(),
-                             n_sink, self.ws_update)
+        fn = P.pbsa_memory_update_shared if shared else P.pbsa_memory_update
+        fn(self.prob, self.kv, t["mass_pool"] if self.C > 0 else None,
+           t["mass_win"] if self.W > 0 else None, leaving, leaving.numel(), n_sink, self.ws_update)
 
     def append_window(self, first_slot: int, first_id: int):
         t = self.t

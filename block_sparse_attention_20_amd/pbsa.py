@@ -19,10 +19,11 @@ LIB_PATH = os.path.join(_HERE, "libpbsa.so")
 PBSA_BF16, PBSA_F32 = 0, 1
 PBSA_OP_SELECT, PBSA_OP_FWD, PBSA_OP_BWD, PBSA_OP_UPDATE, PBSA_OP_FINE_MASS = 0, 1, 2, 3, 4
 PBSA_STATUS_POOL_COUNT, PBSA_STATUS_WIN_LEN, PBSA_STATUS_SEL, PBSA_STATUS_SINK = 1, 2, 4, 8
+PBSA_STATUS_SHARED = 16
 
 # every exported symbol declared in include/pbsa.h
 EXPORTS = ("pbsa_select", "pbsa_block_mass", "pbsa_attn_fwd", "pbsa_attn_bwd", "pbsa_memory_update",
-           "pbsa_fine_mass",
+           "pbsa_fine_mass", "pbsa_memory_update_shared",
            "pbsa_block_mean", "pbsa_window_append", "pbsa_workspace_size", "pbsa_validate",
            "pbsa_strerror", "pbsa_last_error")
 
@@ -75,6 +76,7 @@ def lib() -> ctypes.CDLL:
             "pbsa_attn_bwd": (ctypes.c_int, [P, vp, K, vp, vp, vp, vp, vp, vp, G, vp, sz, vp]),
             "pbsa_memory_update": (ctypes.c_int, [P, K, vp, vp, vp, i32, i64, vp, sz, vp]),
             "pbsa_fine_mass": (ctypes.c_int, [P, vp, K, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "pbsa_memory_update_shared": (ctypes.c_int, [P, K, vp, vp, vp, i32, i64, vp, sz, vp]),
             "pbsa_block_mean": (ctypes.c_int, [P, vp, vp, i64, vp, vp]),
             "pbsa_window_append": (ctypes.c_int, [P, K, vp, vp, vp, vp, vp, i32, i64, vp]),
             "pbsa_workspace_size": (sz, [P, ctypes.c_int]),
@@ -166,6 +168,14 @@ def pbsa_fine_mass(prob, q, kv: KV, sel, sel_count, lse, mass_pool, mass_win, ws
                                 _p(lse), _p(mass_pool), _p(mass_win), _p(ws),
                                 0 if ws is None else ws.numel() * ws.element_size(),
                                 _stream(stream)))
+
+
+def pbsa_memory_update_shared(prob, kv: KV, mass_pool, mass_win, leaving, n_leave, n_sink, ws,
+                              stream=None):
+    _check(lib().pbsa_memory_update_shared(ctypes.byref(prob), ctypes.byref(kv), _p(mass_pool),
+                                           _p(mass_win), _p(leaving), int(n_leave), int(n_sink),
+                                           _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                           _stream(stream)))
 
 
 def pbsa_block_mass(prob, mass_pool, mass_win, ws, stream=None):

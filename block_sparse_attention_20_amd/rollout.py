@@ -20,7 +20,9 @@ The state of a layer is plain device tensors (``PBSALayer.t``), so it can be
 saved and restored with ``state_dict`` / ``load_state_dict``.
 
 With ``mass="fine"`` the update ranks blocks by their exact attention mass
-(pbsa_fine_mass, from the forward's lse) instead of the coarse mass.
+(pbsa_fine_mass, from the forward's lse) instead of the coarse mass; with
+``shared_pool=True`` all heads of a layer keep one pool, ranked by the masses
+summed over heads (pbsa_memory_update_shared).
 
 With ``overlap=True`` steps 2-3 go to a side stream: the next layer needs
 only this layer's output O, while the masses and the updated pool and window
@@ -45,10 +47,12 @@ STATE_KEYS = ("k_win", "v_win", "win_len", "win_id", "kbar_win", "k_pool", "v_po
 class Rollout:
     def __init__(self, n_layers: int, B: int, H: int, d: int, T: int, Nq: int, C: int, topk: int,
                  n_sink: int = 0, window_chunks: int = 2, dtype=torch.bfloat16, scale: float = 0.0,
-                 device="cuda", overlap: bool = False, mass: str = "coarse"):
+                 device="cuda", overlap: bool = False, mass: str = "coarse",
+                 shared_pool: bool = False):
         if mass not in ("coarse", "fine"):
             raise ValueError(f"mass must be 'coarse' or 'fine', not {mass!r}")
         self.mass = mass
+        self.shared_pool = shared_pool
         self.QB = (Nq + T - 1) // T
         self.window_chunks = window_chunks
         self.W = window_chunks * self.QB
@@ -115,7 +119,7 @@ class Rollout:
                 L.fine_mass()        # reads this chunk's lse
             elif self.side is not None or self.mass == "fine":
                 L.block_mass()       # coarse masses from the select scores
-            L.update(self.leaving[t % self.window_chunks], self.n_sink)
+            L.update(self.leaving[t % self.window_chunks], self.n_sink, shared=self.shared_pool)
         L.append_window(self.first_slot(t), t * self.QB)
 
     def sync_side(self):

@@ -82,7 +82,8 @@ enum {
   PBSA_STATUS_POOL_COUNT = 1,  /* pool_count outside [0, C]: clamped */
   PBSA_STATUS_WIN_LEN = 2,     /* a win_len / pool_len outside [0, T]: clamped */
   PBSA_STATUS_SEL = 4,         /* sel entry outside [0, W) or sel_count > topk: skipped/clamped */
-  PBSA_STATUS_SINK = 8         /* more pinned sink blocks than C: kept the C smallest ids */
+  PBSA_STATUS_SINK = 8,        /* more pinned sink blocks than C: kept the C smallest ids */
+  PBSA_STATUS_SHARED = 16      /* head-shared update: the heads of a batch element hold different pools */
 };
 
 typedef struct {
@@ -228,6 +229,22 @@ int pbsa_fine_mass(const pbsa_problem *p, const void *q, const pbsa_kv *kv, cons
 int pbsa_memory_update(const pbsa_problem *p, const pbsa_kv *kv, const float *mass_pool,
                        const float *mass_win, const int32_t *leaving, int32_t n_leave,
                        int64_t n_sink, void *ws, size_t ws_bytes, pbsa_stream_t stream);
+
+/*
+ * pbsa_memory_update_shared - the same update with a head-shared pool (a
+ * policy variant the pages leave open; same section): every head of a batch
+ * element ranks the candidates by the block's mass summed over the heads
+ * (slot-wise for pool blocks, window slots are shared), in ascending head
+ * order, so all heads make the same decision and keep the same blocks in the
+ * same slots.  Precondition: the heads of each batch element hold the same
+ * pool (count and ids), as after every update so far being shared; a
+ * violation sets PBSA_STATUS_SHARED in dev_status (checked when dev_status is
+ * given) and the heads then decide on sums of different blocks' masses.
+ * Arguments, workspace and copies as pbsa_memory_update.
+ */
+int pbsa_memory_update_shared(const pbsa_problem *p, const pbsa_kv *kv, const float *mass_pool,
+                              const float *mass_win, const int32_t *leaving, int32_t n_leave,
+                              int64_t n_sink, void *ws, size_t ws_bytes, pbsa_stream_t stream);
 
 /*
  * pbsa_block_mean - pooled representative (mean of the valid rows) of

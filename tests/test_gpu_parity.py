@@ -295,6 +295,48 @@ def test_memory_update_matches_oracle():
     assert L.status_bits() == 0
 
 
+def test_memory_update_shared_matches_oracle():
+    """Head-shared pool: every head ranks by the masses summed over heads
+    and all heads end with the same pool.  The oracle decides on the same
+    fp32 sums the kernel forms (ascending head order), so near-ties order
+    alike; the oracle's own head summation agrees with them to rounding."""
+    shape = syn.Shape(B=2, H=3, d=128, T=128, Nq=300, W=8, C=5, topk=3)
+    st = syn.make_state(shape, 7, sigma=1.0, shift=1.0, n_planted=3,
+                        win_len=[128, 128, 44, 128, 0, 128, 128, 17], pool_count=4,
+                        pool_len=[128, 128, 100, 128, 128], pool_id=list(range(5)),
+                        win_id=list(range(10, 18)))
+    L = run(shape, st)
+    leaving = [0, 1, 2, 3, 4, 7, 2]
+    mp = L.t["mass_pool"].cpu().numpy(); mw = L.t["mass_win"].cpu().numpy()
+    kbw = L.t["kbar_win"].cpu().numpy(); kbp = L.t["kbar_pool"].cpu().numpy()
+    L.update(torch.tensor(leaving, dtype=torch.int32, device="cuda"), n_sink=1, shared=True)
+    torch.cuda.synchronize()
+    # the kernel's fp32 sums, broadcast to every head
+    sp = np.zeros_like(mp); sw = np.zeros_like(mw)
+    for b in range(shape.B):
+        accp = np.zeros(shape.C, np.float32); accw = np.zeros(shape.W, np.float32)
+        for h in range(shape.H):
+            accp = (accp + mp[b, h]).astype(np.float32); accw = (accw + mw[b, h]).astype(np.float32)
+        sp[b] = accp; sw[b] = accw
+    ref_p, ref_w = po.head_shared_masses(st, mp, mw)
+    np.testing.assert_allclose(ref_p[:, :, :4], sp[:, :, :4], rtol=1e-6)
+    np.testing.assert_allclose(ref_w, sw, rtol=1e-6)
+    u = po.memory_update(st, sp, sw, leaving, 1, kbar_win=kbw, kbar_pool=kbp)
+    np.testing.assert_array_equal(L.t["pool_count"].cpu().numpy(), u["pool_count"])
+    for b, h in np.ndindex(shape.B, shape.H):
+        n = u["pool_count"][b, h]
+        np.testing.assert_array_equal(L.t["pool_id"][b, h, :n].cpu().numpy(), u["pool_id"][b, h, :n])
+        np.testing.assert_array_equal(L.t["pool_id"][b, h].cpu().numpy(), L.t["pool_id"][b, 0].cpu().numpy())
+        for slot, w in u["admitted"][(b, h)]:
+            assert torch.equal(L.t["k_pool"][b, h, slot], L.t["k_win"][b, h, w])
+    assert L.status_bits() == 0
+    # heads that disagree are flagged
+    L.t["pool_id"][1, 2, 0] = 99
+    L.update(torch.tensor([5], dtype=torch.int32, device="cuda"), shared=True)
+    torch.cuda.synchronize()
+    assert L.status_bits() & P.PBSA_STATUS_SHARED
+
+
 def test_window_append_copies_chunk():
     shape = syn.Shape(B=1, H=2, d=64, T=64, Nq=150, W=6, C=1, topk=1)
     st = syn.make_state(shape, 2, win_len=[64, 64, 22, 0, 0, 0], pool_count=1)
