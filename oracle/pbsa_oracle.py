@@ -48,6 +48,9 @@ each reading is tagged R<n> and listed with its basis in the design notes:
   R15 placement: survivors keep their slots; freed slots, then the unused
       tail, are filled in ascending order by the admitted blocks in
       ascending id order; valid pool slots are always [0, count)
+  R21 training through a rollout: the routing and pool decisions of every
+      chunk are held fixed; a stored block's gradient belongs to the rows of
+      the chunk that produced it
   R20 head-shared pool (a policy variant): every head of a batch element
       ranks the candidates by the block's masses summed over the heads
   R19 fine-grained block mass (an alternative to R11's coarse mass): the

@@ -86,3 +86,70 @@ class OracleRollout:
             self.win_id[w] = t * self.QB + j
         self.t += 1
         return out
+
+
+# ----------------------------------------------------------------------------
+# Training through a rollout (R21): the loss sum_t <dO_t, O_t> differentiated
+# through every chunk's attention with the routing and pool decisions held
+# fixed (stop-gradient, as for the single-chunk backward).  A stored block is
+# a copy of rows of the chunk that produced it (R14), so the gradient a pool
+# or window slot receives belongs to those rows of that chunk's K/V.
+# ----------------------------------------------------------------------------
+def _history_rows(x: np.ndarray, ids, Nq: int, T: int, QB: int, b: int, h: int) -> tuple:
+    """Rows of the history blocks `ids` (block id c*QB + j = rows
+    [j T, min(Nq, (j+1) T)) of chunk c), concatenated, and their
+    (chunk, row) origins."""
+    rows, origin = [], []
+    for x_id in ids:
+        c, j = divmod(int(x_id), QB)
+        r0, r1 = j * T, min(Nq, (j + 1) * T)
+        rows.append(x[c][b, h, r0:r1])
+        origin += [(c, r) for r in range(r0, r1)]
+    if not rows:
+        return np.zeros((0, x[0].shape[-1])), origin
+    return np.concatenate(rows, axis=0), origin
+
+
+def rollout_attention_grads(q: list, k: list, v: list, plans: list, dout: list, scale: float,
+                            T: int) -> dict:
+    """Gradients of L = sum_t sum_rows <dO_t, O_t> over the chunks of a
+    rollout.  q, k, v, dout: per chunk [B,H,Nq,d] arrays; plans[t][b][h][i]:
+    the history block ids query block i of chunk t attends (pool blocks and
+    selected window blocks); chunk t itself is attended in full.  Returns
+    per-chunk dq, dk, dv (fp64) and the outputs o."""
+    q = [po._f64(x) for x in q]; k = [po._f64(x) for x in k]
+    v = [po._f64(x) for x in v]; dout = [po._f64(x) for x in dout]
+    n = len(q)
+    B, H, Nq, d = q[0].shape
+    QB = po.n_blocks(Nq, T)
+    dq = [np.zeros_like(x) for x in q]
+    dk = [np.zeros_like(x) for x in k]
+    dv = [np.zeros_like(x) for x in v]
+    o = [np.zeros_like(x) for x in q]
+    for t in range(n):
+        for b in range(B):
+            for h in range(H):
+                for i in range(QB):
+                    r0, r1 = i * T, min(Nq, (i + 1) * T)
+                    ids = plans[t][b][h][i]
+                    Kh, org = _history_rows(k, ids, Nq, T, QB, b, h)
+                    Vh, _ = _history_rows(v, ids, Nq, T, QB, b, h)
+                    K = np.concatenate([Kh, k[t][b, h]], axis=0)
+                    V = np.concatenate([Vh, v[t][b, h]], axis=0)
+                    org = org + [(t, r) for r in range(Nq)]
+                    Q = q[t][b, h, r0:r1]
+                    dO = dout[t][b, h, r0:r1]
+                    z = scale * (Q @ K.T)
+                    e = np.exp(z - z.max(axis=1, keepdims=True))
+                    P = e / e.sum(axis=1, keepdims=True)
+                    O = P @ V
+                    o[t][b, h, r0:r1] = O
+                    Dr = (dO * O).sum(axis=1, keepdims=True)
+                    dS = P * (dO @ V.T - Dr)
+                    dq[t][b, h, r0:r1] += scale * (dS @ K)
+                    dK = scale * (dS.T @ Q)
+                    dV = P.T @ dO
+                    for u, (c, r) in enumerate(org):
+                        dk[c][b, h, r] += dK[u]
+                        dv[c][b, h, r] += dV[u]
+    return dict(dq=dq, dk=dk, dv=dv, o=o)

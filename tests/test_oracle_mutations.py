@@ -8,6 +8,7 @@ import textwrap
 import pytest
 
 from oracle import pbsa_oracle as po
+from oracle import rollout as orl
 import test_oracle_pins as pins
 
 # (function, source fragment, planted replacement, pins expected to catch it)
@@ -54,6 +55,13 @@ MUTATIONS = [
     ("head_shared_masses", "tot[x] = tot.get(x, 0.0) + float(mass_pool[b, h, p])",
      "tot[x] = float(mass_pool[b, h, p])",
      ["test_update_head_shared_pool_is_best_subset_of_summed_mass"]),
+    ("rollout.rollout_attention_grads", "dk[c][b, h, r] += dK[u]", "dk[t][b, h, r % Nq] += dK[u]",
+     ["test_rollout_grads_match_autograd_of_flat_masked_attention"]),
+    ("rollout.rollout_attention_grads", "dS = P * (dO @ V.T - Dr)", "dS = P * (dO @ V.T)",
+     ["test_rollout_grads_match_autograd_of_flat_masked_attention",
+      "test_rollout_grads_single_chunk_is_the_chunk_backward"]),
+    ("rollout._history_rows", "r0, r1 = j * T, min(Nq, (j + 1) * T)", "r0, r1 = j * T, (j + 1) * T",
+     ["test_rollout_grads_match_autograd_of_flat_masked_attention"]),
     ("memory_update_one", "free = sorted(free)", "free = sorted(free, reverse=True)",
      ["test_update_placement_golden"]),
     ("memory_update_one", "admitted = sorted([x for x in kept if x[0] == \"cand\"], key=lambda x: x[2])",
@@ -64,18 +72,25 @@ MUTATIONS = [
 ]
 
 
+def _module(fn_name):
+    """'rollout.f' names a function of oracle/rollout.py, 'f' one of pbsa_oracle."""
+    return (orl, fn_name.split(".", 1)[1]) if fn_name.startswith("rollout.") else (po, fn_name)
+
+
 def _mutated(fn_name, old, new):
-    src = textwrap.dedent(inspect.getsource(getattr(po, fn_name)))
+    mod, name = _module(fn_name)
+    src = textwrap.dedent(inspect.getsource(getattr(mod, name)))
     assert old in src, (fn_name, old)
-    ns = dict(vars(po))
+    ns = dict(vars(mod))
     exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
-    return ns[fn_name]
+    return ns[name]
 
 
 @pytest.mark.parametrize("fn_name,old,new,catchers", MUTATIONS,
                          ids=[f"{m[0]}:{i}" for i, m in enumerate(MUTATIONS)])
 def test_pins_catch_planted_mistakes(monkeypatch, fn_name, old, new, catchers):
-    monkeypatch.setattr(po, fn_name, _mutated(fn_name, old, new))
+    mod, name = _module(fn_name)
+    monkeypatch.setattr(mod, name, _mutated(fn_name, old, new))
     caught = []
     for name in catchers:
         name, kwargs = name if isinstance(name, tuple) else (name, {})

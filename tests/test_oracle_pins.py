@@ -16,6 +16,7 @@ import torch
 
 import pbsa_synth as syn
 from oracle import pbsa_oracle as po
+from oracle import rollout as orl
 from oracle.rollout import OracleRollout
 
 
@@ -428,6 +429,63 @@ def test_fine_mass_matches_bruteforce_token_mask(T, d):
         np.testing.assert_allclose(f["mass_cur"][0, h],
                                    [cur[c * T:(c + 1) * T].sum() for c in range(4)],
                                    rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------- training through a rollout ---
+def _random_rollout(n, B, H, d, T, Nq, seed):
+    g = torch.Generator().manual_seed(seed)
+    QB = -(-Nq // T)
+    mk = lambda: [torch.randn(B, H, Nq, d, generator=g, dtype=torch.float64) for _ in range(n)]
+    q, k, v, dout = mk(), mk(), mk(), mk()
+    rng = np.random.default_rng(seed)
+    plans = [[[[sorted(int(x) for x in rng.choice(t * QB, size=rng.integers(0, t * QB + 1),
+                                                   replace=False)) if t else []
+                for _ in range(QB)] for _ in range(H)] for _ in range(B)] for t in range(n)]
+    return q, k, v, dout, plans, QB
+
+
+def test_rollout_grads_match_autograd_of_flat_masked_attention():
+    # every chunk's keys on one flat axis [chunk 0 | chunk 1 | ...]; a query
+    # row of chunk t sees its planned history blocks and all of chunk t; torch
+    # autograd of sum <dO, O> is the reference
+    n, B, H, d, T, Nq = 4, 1, 2, 4, 2, 5
+    q, k, v, dout, plans, QB = _random_rollout(n, B, H, d, T, Nq, 11)
+    scale = 0.6
+    r = orl.rollout_attention_grads([x.numpy() for x in q], [x.numpy() for x in k],
+                                [x.numpy() for x in v], plans, [x.numpy() for x in dout], scale, T)
+    qs = [x.clone().requires_grad_() for x in q]
+    K = torch.cat([x.clone() for x in k], dim=2).requires_grad_()
+    V = torch.cat([x.clone() for x in v], dim=2).requires_grad_()
+    loss = 0
+    for t in range(n):
+        mask = torch.zeros(B, H, Nq, n * Nq, dtype=torch.bool)
+        for b, h, row in itertools.product(range(B), range(H), range(Nq)):
+            for x_id in plans[t][b][h][row // T]:
+                c, j = divmod(x_id, QB)
+                mask[b, h, row, c * Nq + j * T:c * Nq + min(Nq, (j + 1) * T)] = True
+            mask[b, h, row, t * Nq:(t + 1) * Nq] = True
+        z = scale * qs[t] @ K.transpose(-1, -2)
+        P = torch.softmax(z.masked_fill(~mask, float("-inf")), dim=-1)
+        loss = loss + (dout[t] * (P @ V)).sum()
+    loss.backward()
+    for t in range(n):
+        np.testing.assert_allclose(r["dq"][t], qs[t].grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(r["dk"][t], K.grad[:, :, t * Nq:(t + 1) * Nq].numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(r["dv"][t], V.grad[:, :, t * Nq:(t + 1) * Nq].numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_rollout_grads_single_chunk_is_the_chunk_backward():
+    n, B, H, d, T, Nq = 1, 1, 2, 8, 4, 10
+    q, k, v, dout, plans, QB = _random_rollout(n, B, H, d, T, Nq, 3)
+    r = orl.rollout_attention_grads([x.numpy() for x in q], [x.numpy() for x in k],
+                                [x.numpy() for x in v], plans, [x.numpy() for x in dout], 0.4, T)
+    shape = syn.Shape(B=B, H=H, d=d, T=T, Nq=Nq, W=0, C=0, topk=0, dtype=torch.float32)
+    st = syn.make_state(shape, 0, win_len=[], pool_count=0)
+    st["q"], st["k_cur"], st["v_cur"] = q[0], k[0], v[0]
+    g = po.attn_bwd(st, np.zeros((B, H, QB, 1), int), np.zeros((B, H, QB), int), dout[0].numpy(), 0.4, T)
+    np.testing.assert_allclose(r["dq"][0], g["dq"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["dk"][0], g["dk_cur"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["dv"][0], g["dv_cur"], rtol=1e-12, atol=1e-12)
 
 
 # ----------------------------------------------------------- memory update ---
