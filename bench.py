@@ -416,6 +416,71 @@ def mass_compare(torch, n_chunks=16, n_layers=2, device="cuda"):
             "per_chunk": rows, "fine_mass_us": round(e0.elapsed_time(e1) * 1e3 / 20, 1)}
 
 
+def train_rollout_bench(torch, n_chunks=8, device="cuda"):
+    """Training through a streaming rollout in the Wan shape (one layer,
+    12 heads x 128, 4680-token chunks, window of 2 chunks, pool cap 64,
+    top-16): the forward over n_chunks records routing and pool decisions;
+    the backward runs, per chunk, pbsa_block_gather of the attended pool and
+    window slots, pbsa_attn_bwd and pbsa_grad_scatter into fp32 history
+    gradients.  HIP events around each chunk's forward and backward, and
+    around the gather / scatter calls alone."""
+    import pbsa_synth as syn
+    from block_sparse_attention_20_amd import pbsa as P
+    from block_sparse_attention_20_amd.train import TrainRollout
+    s = syn.WAN_CHUNK
+    C = syn.ROLLOUT_POOL_CAP
+    shape = syn.Shape(B=s.B, H=s.H, d=s.d, T=s.T, Nq=s.Nq, W=0, C=C, topk=s.topk)
+    sigma = 1 / math.sqrt(s.d)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def run(timed):
+        tr = TrainRollout(n_chunks, s.B, s.H, s.d, s.T, s.Nq, C, s.topk, device=device)
+        fwd = []
+        douts = []
+        for t in range(n_chunks):
+            u = syn.rollout_direction(5, 0, t, s.d, device=device)
+            ch = syn.make_chunk(shape, syn.rollout_seed(5, 0, t), u, sigma=sigma, shift=1.5,
+                                n_planted=8, device=device)
+            douts.append(syn.make_dout(shape, 9000 + t, device=device))
+            a, b = ev()
+            a.record(); tr.forward(ch["q"], ch["k"], ch["v"]); b.record()
+            fwd.append((a, b))
+        torch.cuda.synchronize()
+        a, b = ev()
+        a.record(); tr.backward(douts); b.record()
+        torch.cuda.synchronize()
+        return tr, [x.elapsed_time(y) for x, y in fwd], a.elapsed_time(b), douts
+
+    run(False)  # warm-up (first launches, allocator)
+    tr, fwd_ms, bwd_ms, douts = run(True)
+    # gather + scatter alone, on the last chunk's record, repeated
+    r, D = tr.rec[-1], tr.D
+    g = D.bwd(douts[-1])
+    gk = torch.zeros(n_chunks, s.B, s.H, s.Nq, s.d, dtype=torch.float32, device=device)
+    gv = torch.zeros_like(gk)
+    a, b = ev()
+    a.record()
+    for _ in range(10):
+        P.pbsa_block_gather(D.prob, r["win_id"], 0, None, tr.W, tr.k_hist, tr.v_hist, n_chunks,
+                            D.t["k_win"], D.t["v_win"], None)
+        P.pbsa_block_gather(D.prob, r["pool_id"], C, r["pool_count"], C, tr.k_hist, tr.v_hist,
+                            n_chunks, D.t["k_pool"], D.t["v_pool"], D.t["pool_len"])
+        P.pbsa_grad_scatter(D.prob, r["win_id"], 0, None, tr.W, 0, g["dk_win"], g["dv_win"], gk, gv,
+                            n_chunks)
+        P.pbsa_grad_scatter(D.prob, r["pool_id"], C, r["pool_count"], C, 0, g["dk_pool"], g["dv_pool"],
+                            gk, gv, n_chunks)
+    b.record()
+    torch.cuda.synchronize()
+    return {"workload": f"training through a streaming rollout, {n_chunks} chunks of the Wan "
+                        f"shape, one layer, pool cap {C}",
+            "fwd_ms_per_chunk": [round(x, 3) for x in fwd_ms],
+            "bwd_ms_total": round(bwd_ms, 3),
+            "bwd_ms_per_chunk": round(bwd_ms / n_chunks, 3),
+            "gather_scatter_ms_per_chunk": round(a.elapsed_time(b) / 10, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -428,6 +493,8 @@ def main():
     ap.add_argument("--no-rollout", action="store_true", help="skip the 20 s / 1 min rollouts")
     ap.add_argument("--sweep", action="store_true",
                     help="only the sparsity x history sweep of the forward (its own JSON line)")
+    ap.add_argument("--train-rollout", action="store_true",
+                    help="only the training-through-a-rollout timing (its own JSON line)")
     ap.add_argument("--mass-compare", action="store_true",
                     help="only the coarse vs exact block-mass comparison (its own JSON line)")
     args = ap.parse_args()
@@ -443,6 +510,9 @@ def main():
     dev = "cuda"
     if args.sweep:
         print(json.dumps({"sweep": sweep(torch, dev)}), flush=True)
+        return
+    if args.train_rollout:
+        print(json.dumps({"train_rollout": train_rollout_bench(torch, device=dev)}), flush=True)
         return
     if args.mass_compare:
         print(json.dumps({"mass_compare": mass_compare(torch, device=dev)}), flush=True)

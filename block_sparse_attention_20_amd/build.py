@@ -14,7 +14,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["pbsa_api.hip", "pbsa_select.hip", "pbsa_attn_fwd.hip", "pbsa_attn_bwd.hip",
-           "pbsa_update.hip", "pbsa_fine_mass.hip"]
+           "pbsa_update.hip", "pbsa_fine_mass.hip", "pbsa_train.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 (the host pass warns that it does
 # not know the feature; that warning is harmless).

@@ -189,6 +189,7 @@ int pbsa_attn_bwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const
                   pbsa_stream_t stream) {
   int rc = check_problem(p, PBSA_OP_BWD);
   if (rc) return rc;
+  if (p->dtype != PBSA_BF16) return fail(PBSA_ERR_UNSUPPORTED, "pbsa_attn_bwd supports bf16 only");
   REQ(q);
   if ((rc = check_kv_common(kv, p))) return rc;
   if (p->topk > 0) REQ(sel);
@@ -266,6 +267,52 @@ int pbsa_memory_update_shared(const pbsa_problem *p, const pbsa_kv *kv, const fl
                               int64_t n_sink, void *ws, size_t ws_bytes, pbsa_stream_t stream) {
   return memory_update_impl(p, kv, mass_pool, mass_win, leaving, n_leave, n_sink, ws, ws_bytes,
                             stream, true);
+}
+
+static int check_slots(const pbsa_problem *p, const int64_t *ids, int64_t ids_bh_stride,
+                       int32_t n_slots, int32_t n_chunks) {
+  if (n_slots < 0 || n_slots > 65535) return fail(PBSA_ERR_SHAPE, "n_slots=%d outside [0, 65535]", n_slots);
+  if (ids_bh_stride != 0 && ids_bh_stride < n_slots)
+    return fail(PBSA_ERR_SHAPE, "ids_bh_stride=%lld must be 0 or >= n_slots=%d",
+                (long long)ids_bh_stride, n_slots);
+  if (n_chunks < 1 || (long long)n_chunks * p->B * p->H * p->Nq > (1LL << 40))
+    return fail(PBSA_ERR_SHAPE, "n_chunks=%d out of range", n_chunks);
+  if (n_slots > 0) REQ(ids);
+  return PBSA_OK;
+}
+
+int pbsa_block_gather(const pbsa_problem *p, const int64_t *ids, int64_t ids_bh_stride,
+                      const int32_t *count, int32_t n_slots, const void *k_hist, const void *v_hist,
+                      int32_t n_chunks, void *k_out, void *v_out, int32_t *len_out,
+                      pbsa_stream_t stream) {
+  int rc = check_problem(p, PBSA_OP_BWD);
+  if (rc) return rc;
+  if ((rc = check_slots(p, ids, ids_bh_stride, n_slots, n_chunks))) return rc;
+  REQ(k_hist);
+  REQ(v_hist);
+  REQ(k_out);
+  REQ(v_out);
+  if (count && !aligned16(count)) return fail(PBSA_ERR_ALIGN, "count is not 16-byte aligned");
+  if (len_out && !aligned16(len_out)) return fail(PBSA_ERR_ALIGN, "len_out is not 16-byte aligned");
+  return hip_status(pbsa::launch_block_gather(*p, ids, ids_bh_stride, count, n_slots, k_hist, v_hist,
+                                              n_chunks, k_out, v_out, len_out, (hipStream_t)stream));
+}
+
+int pbsa_grad_scatter(const pbsa_problem *p, const int64_t *ids, int64_t ids_bh_stride,
+                      const int32_t *count, int32_t n_slots, int32_t src_is_chunk, const void *dk,
+                      const void *dv, float *gk, float *gv, int32_t n_chunks, pbsa_stream_t stream) {
+  int rc = check_problem(p, PBSA_OP_BWD);
+  if (rc) return rc;
+  if ((rc = check_slots(p, ids, ids_bh_stride, n_slots, n_chunks))) return rc;
+  if (src_is_chunk != 0 && src_is_chunk != 1)
+    return fail(PBSA_ERR_SHAPE, "src_is_chunk must be 0 or 1");
+  REQ(dk);
+  REQ(dv);
+  REQ(gk);
+  REQ(gv);
+  if (count && !aligned16(count)) return fail(PBSA_ERR_ALIGN, "count is not 16-byte aligned");
+  return hip_status(pbsa::launch_grad_scatter(*p, ids, ids_bh_stride, count, n_slots, src_is_chunk,
+                                              dk, dv, gk, gv, n_chunks, (hipStream_t)stream));
 }
 
 int pbsa_block_mean(const pbsa_problem *p, const void *x, const int32_t *len, int64_t n_blocks,

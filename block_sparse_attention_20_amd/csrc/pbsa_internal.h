@@ -38,6 +38,14 @@ hipError_t launch_attn_bwd(const pbsa_problem &p, float scale, const void *q, co
 hipError_t launch_fine_mass(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
                             const int32_t *sel, const int32_t *sel_count, const float *lse,
                             float *mass_pool, float *mass_win, void *ws, hipStream_t st);
+hipError_t launch_block_gather(const pbsa_problem &p, const int64_t *ids, int64_t ids_bh_stride,
+                               const int32_t *count, int n_slots, const void *k_hist,
+                               const void *v_hist, int n_chunks, void *k_out, void *v_out,
+                               int32_t *len_out, hipStream_t st);
+hipError_t launch_grad_scatter(const pbsa_problem &p, const int64_t *ids, int64_t ids_bh_stride,
+                               const int32_t *count, int n_slots, int src_is_chunk,
+                               const void *dk, const void *dv, float *gk, float *gv, int n_chunks,
+                               hipStream_t st);
 hipError_t launch_memory_update(const pbsa_problem &p, const pbsa_kv &kv, const float *mass_pool,
                                 const float *mass_win, const int32_t *leaving, int n_leave,
                                 int64_t n_sink, bool shared, void *ws, hipStream_t st);

@@ -23,7 +23,7 @@ PBSA_STATUS_SHARED = 16
 
 # every exported symbol declared in include/pbsa.h
 EXPORTS = ("pbsa_select", "pbsa_block_mass", "pbsa_attn_fwd", "pbsa_attn_bwd", "pbsa_memory_update",
-           "pbsa_fine_mass", "pbsa_memory_update_shared",
+           "pbsa_fine_mass", "pbsa_memory_update_shared", "pbsa_block_gather", "pbsa_grad_scatter",
            "pbsa_block_mean", "pbsa_window_append", "pbsa_workspace_size", "pbsa_validate",
            "pbsa_strerror", "pbsa_last_error")
 
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
             "pbsa_memory_update": (ctypes.c_int, [P, K, vp, vp, vp, i32, i64, vp, sz, vp]),
             "pbsa_fine_mass": (ctypes.c_int, [P, vp, K, vp, vp, vp, vp, vp, vp, sz, vp]),
             "pbsa_memory_update_shared": (ctypes.c_int, [P, K, vp, vp, vp, i32, i64, vp, sz, vp]),
+            "pbsa_block_gather": (ctypes.c_int, [P, vp, i64, vp, i32, vp, vp, i32, vp, vp, vp, vp]),
+            "pbsa_grad_scatter": (ctypes.c_int, [P, vp, i64, vp, i32, i32, vp, vp, vp, vp, i32, vp]),
             "pbsa_block_mean": (ctypes.c_int, [P, vp, vp, i64, vp, vp]),
             "pbsa_window_append": (ctypes.c_int, [P, K, vp, vp, vp, vp, vp, i32, i64, vp]),
             "pbsa_workspace_size": (sz, [P, ctypes.c_int]),
@@ -176,6 +178,20 @@ def pbsa_memory_update_shared(prob, kv: KV, mass_pool, mass_win, leaving, n_leav
                                            _p(mass_win), _p(leaving), int(n_leave), int(n_sink),
                                            _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                            _stream(stream)))
+
+
+def pbsa_block_gather(prob, ids, ids_bh_stride, count, n_slots, k_hist, v_hist, n_chunks, k_out,
+                      v_out, len_out=None, stream=None):
+    _check(lib().pbsa_block_gather(ctypes.byref(prob), _p(ids), int(ids_bh_stride), _p(count),
+                                   int(n_slots), _p(k_hist), _p(v_hist), int(n_chunks), _p(k_out),
+                                   _p(v_out), _p(len_out), _stream(stream)))
+
+
+def pbsa_grad_scatter(prob, ids, ids_bh_stride, count, n_slots, src_is_chunk, dk, dv, gk, gv,
+                      n_chunks, stream=None):
+    _check(lib().pbsa_grad_scatter(ctypes.byref(prob), _p(ids), int(ids_bh_stride), _p(count),
+                                   int(n_slots), int(src_is_chunk), _p(dk), _p(dv), _p(gk), _p(gv),
+                                   int(n_chunks), _stream(stream)))
 
 
 def pbsa_block_mass(prob, mass_pool, mass_win, ws, stream=None):

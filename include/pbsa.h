@@ -46,8 +46,9 @@
  *
  * Supported: dtype PBSA_BF16 with d in {64, 128} and T in {64, 128}
  * (bf16 MFMA, fp32 accumulate and softmax); dtype PBSA_F32 with d in
- * {64, 128}, T in {64, 128} (fp32 vector path).  W <= 1024, C <= 1024,
- * 0 <= topk <= W.
+ * {64, 128}, T in {64, 128} (fp32 vector path) for every call except
+ * pbsa_attn_bwd, which is bf16 only (PBSA_ERR_UNSUPPORTED otherwise).
+ * W <= 1024, C <= 1024, 0 <= topk <= W.
  */
 #ifndef PBSA_H
 #define PBSA_H
@@ -183,7 +184,7 @@ int pbsa_attn_fwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const
  * dS = P (dO V^T - D):  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO,
  * each landing on the storage slot of its token.  Every element of every
  * gradient buffer is written (zero where no query attends).  dq and every
- * pbsa_kv_grad field are required.
+ * pbsa_kv_grad field are required.  bf16 only.
  * Workspace: pbsa_workspace_size(p, PBSA_OP_BWD) bytes.
  */
 int pbsa_attn_bwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const int32_t *sel,
@@ -245,6 +246,40 @@ int pbsa_memory_update(const pbsa_problem *p, const pbsa_kv *kv, const float *ma
 int pbsa_memory_update_shared(const pbsa_problem *p, const pbsa_kv *kv, const float *mass_pool,
                               const float *mass_win, const int32_t *leaving, int32_t n_leave,
                               int64_t n_sink, void *ws, size_t ws_bytes, pbsa_stream_t stream);
+
+/*
+ * Training through a streaming rollout (the sparse attention is trainable;
+ * same pages).  A pool or window slot holds a copy of block j of an earlier
+ * chunk c, block id c*QB + j: rows [j T, min(Nq, (j+1) T)) of that chunk's
+ * K and V.  With the routing and pool decisions of every chunk held fixed,
+ * the gradient a slot receives in pbsa_attn_bwd belongs to those rows.
+ * History and gradient accumulators hold all chunks of the rollout:
+ * k_hist / v_hist [n_chunks,B,H,Nq,d] in the problem dtype, gk / gv
+ * [n_chunks,B,H,Nq,d] fp32.  Slot ids: ids[(b*H + h) * ids_bh_stride + s]
+ * for slot s (ids_bh_stride 0: one list for every (b, h), as for the window;
+ * otherwise >= n_slots); id < 0 = empty slot; count (optional, [B,H]) makes
+ * the slots >= count[b,h] empty.  An id whose chunk is >= n_chunks is
+ * treated as empty and sets PBSA_STATUS_SEL.
+ *
+ * pbsa_block_gather - rebuild slots from the history: k_out / v_out
+ * [B,H,n_slots,T,d] get the block's rows, zeros after its length (empty
+ * slots: all zeros); len_out (optional, [B,H,n_slots] int32) its length.
+ *
+ * pbsa_grad_scatter - gk[c][b,h,rows] += dk of the slot (and gv, dv): with
+ * src_is_chunk = 0, dk / dv are slot-shaped [B,H,n_slots,T,d] (the pool or
+ * window gradients of pbsa_attn_bwd); with src_is_chunk = 1 they are
+ * chunk-shaped [B,H,Nq,d] and block j's rows are read at j T (the chunk's own
+ * dk_cur / dv_cur, ids c*QB + j).  The non-negative ids of one (b, h) must be
+ * distinct within a call (each destination row is added by one workgroup);
+ * successive calls accumulate in call order.
+ */
+int pbsa_block_gather(const pbsa_problem *p, const int64_t *ids, int64_t ids_bh_stride,
+                      const int32_t *count, int32_t n_slots, const void *k_hist, const void *v_hist,
+                      int32_t n_chunks, void *k_out, void *v_out, int32_t *len_out,
+                      pbsa_stream_t stream);
+int pbsa_grad_scatter(const pbsa_problem *p, const int64_t *ids, int64_t ids_bh_stride,
+                      const int32_t *count, int32_t n_slots, int32_t src_is_chunk, const void *dk,
+                      const void *dv, float *gk, float *gv, int32_t n_chunks, pbsa_stream_t stream);
 
 /*
  * pbsa_block_mean - pooled representative (mean of the valid rows) of

@@ -127,4 +127,15 @@ def test_entry_points_reject_before_launch():
                             need, None) == -1
     assert L.pbsa_fine_mass(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, fake, fake, fake,
                             need - 1, None) == -5
+    # gather / scatter: slot counts, id strides, chunk counts, required pointers
+    assert L.pbsa_block_gather(ctypes.byref(p), fake, 0, None, 70000, fake, fake, 2, fake, fake, None, None) == -2
+    assert L.pbsa_block_gather(ctypes.byref(p), fake, 3, None, 4, fake, fake, 2, fake, fake, None, None) == -2
+    assert L.pbsa_block_gather(ctypes.byref(p), fake, 0, None, 4, fake, fake, 0, fake, fake, None, None) == -2
+    assert L.pbsa_block_gather(ctypes.byref(p), None, 0, None, 4, fake, fake, 2, fake, fake, None, None) == -1
+    assert L.pbsa_grad_scatter(ctypes.byref(p), fake, 0, None, 4, 2, fake, fake, fake, fake, 2, None) == -2
+    assert L.pbsa_grad_scatter(ctypes.byref(p), fake, 0, None, 4, 0, fake, fake, None, fake, 2, None) == -1
+    # the backward is bf16 only, refused on the host
+    f32 = wan(); f32.dtype = P.PBSA_F32
+    assert L.pbsa_attn_bwd(ctypes.byref(f32), fake, ctypes.byref(kv2), fake, fake, fake, fake, fake, fake,
+                           ctypes.byref(g), fake, 1 << 30, None) == -7
     assert L.pbsa_strerror(-5).decode().startswith("workspace")
