@@ -40,8 +40,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # FETCH 14,167 KiB, WRITE 28,304 KiB).  Valid only for the kernel source it
 # was measured on (sha1 over FWD_SOURCES below); reported as null once those
 # sources change.
-FWD_TRAFFIC = {"src_sha1": "ed642f70eca7328a1ac1ba9854cea02010b6df1a",
-               "fetch_kib": 60227.5, "write_kib": 14259.9,
+FWD_TRAFFIC = {"src_sha1": "cee553ba2d23046dd1f06a788f1acde8a93f5939",
+               "fetch_kib": 60229.9, "write_kib": 14259.9,
                "fetch_scale": 28302.0 / 14166.7, "write_scale": 28302.0 / 28304.3}
 
 

@@ -16,17 +16,20 @@
 //     16-byte chunks are XOR-swizzled per row; each buffer descriptor covers
 //     only the valid rows, so lanes past them write zeros and padding can
 //     never inject NaN;
-//   - the next block's K is in flight while the softmax and P V of the
-//     current block run, and its V while the next S is computed (one K and
-//     one V buffer, four barriers per block);
+//   - the list is walked in 64-token tiles, double buffered (separate K0/K1,
+//     V0/V1 arrays indexed at compile time), one barrier per tile: the next
+//     tile's DMA is issued one instruction per k-step of the current tile's
+//     S MFMAs;
 //   - S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q held
 //     in registers for the whole kernel), so each lane owns one query column
-//     and the row softmax is in-lane plus one cross-half exchange;
+//     and the row softmax is in-lane (four independent max chains) plus one
+//     lane-half swap (v_permlane32_swap);
 //   - online softmax in the log2 domain; the running max only moves when a
 //     block raises it by more than 8 (P <= 2^8), so O is rarely rescaled;
 //   - P is rounded to bf16 in registers and is directly the B operand of
 //     O^T = V^T P^T; the V^T A operand is read from the row-major V tile with
-//     ds_read_b64_tr_b16 (two 4x16 transposed reads per fragment);
+//     ds_read_b64_tr_b16 (two 4x16 transposed reads per fragment); this part
+//     runs at raised wave priority;
 //   - work items are mapped XCD-aware: consecutive query blocks of a head
 //     run on the same XCD and share its L2 for the pool/current K/V.
 // fp32 path: plain vector FMA version of the same walk (small problems).
