@@ -398,12 +398,24 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dq_kernel(BwdAr
         f32x16 sacc, pacc;
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[e] = pacc[e] = 0.f;
+        // K / V fragments read PD k-steps ahead of their MFMAs (an empty asm
+        // on each keeps the MFMA behind the reads)
+        constexpr int PD = 2;
+        bf16x8 kfr[PD + 1], vfr[PD + 1];
+#pragma unroll
+        for (int k0 = 0; k0 < PD; ++k0) {
+          kfr[k0] = *reinterpret_cast<const bf16x8 *>(&Kl[hf * 32 * D + koff[k0]]);
+          vfr[k0] = *reinterpret_cast<const bf16x8 *>(&Vl[hf * 32 * D + voff[k0]]);
+        }
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&Kl[hf * 32 * D + koff[kk]]);
-          const bf16x8 va = *reinterpret_cast<const bf16x8 *>(&Vl[hf * 32 * D + voff[kk]]);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc, 0, 0, 0);
-          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[kk], pacc, 0, 0, 0);
+          if (kk + PD < D / 16) {
+            kfr[(kk + PD) % (PD + 1)] = *reinterpret_cast<const bf16x8 *>(&Kl[hf * 32 * D + koff[kk + PD]]);
+            vfr[(kk + PD) % (PD + 1)] = *reinterpret_cast<const bf16x8 *>(&Vl[hf * 32 * D + voff[kk + PD]]);
+          }
+          asm volatile("" : "+v"(kfr[kk % (PD + 1)]), "+v"(vfr[kk % (PD + 1)]));
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[kk % (PD + 1)], qf[kk], sacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[kk % (PD + 1)], df[kk], pacc, 0, 0, 0);
         }
         // the exponentials and dQ MFMAs run at raised wave priority (as in
         // the forward: the other workgroup's S / dP MFMAs fill around them)
