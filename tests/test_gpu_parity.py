@@ -443,3 +443,46 @@ def test_fine_mass_wan_chunk_full_size(unscaled):
     planted = st["planted"]
     others = [w for w in range(shape.W) if w not in planted]
     assert mw[0][:, planted].min() > mw[0][:, others].max()
+
+
+def test_maximum_sizes():
+    """W = C = 1024 (the largest window and pool), k = 1000: routing, the
+    forward over 2,026 blocks per query block, exact masses and a full
+    update (1,024 pool blocks + 1,024 leaving candidates) against the oracle."""
+    shape = syn.Shape(B=1, H=1, d=64, T=64, Nq=2 * 64 - 9, W=1024, C=1024, topk=1000)
+    wl = [64] * 1024
+    wl[5] = 0; wl[700] = 13
+    pl = [64] * 1024
+    pl[3] = 40
+    st = syn.make_state(shape, 17, sigma=1.0, shift=1.0, n_planted=6, win_len=wl, pool_count=1024,
+                        pool_len=pl, win_id=list(range(2000, 3024)))
+    _log("max sizes: select + fwd")
+    L = run(shape, st)
+    scale = eff_scale(shape, 0.0)
+    r = po.select(st, shape.topk, scale, shape.T)
+    check_selection(L, r, st, shape.topk)
+    np.testing.assert_allclose(L.t["mass_pool"].cpu().numpy(), r["mass_pool"], rtol=1e-4, atol=1e-6)
+    np.testing.assert_allclose(L.t["mass_win"].cpu().numpy(), r["mass_win"], rtol=1e-4, atol=1e-6)
+    gsel = L.t["sel"].cpu().numpy(); gcnt = L.t["sel_count"].cpu().numpy()
+    f = po.attn_fwd(st, gsel, gcnt, scale, shape.T)
+    check_close_bf16(L.t["o"].float().cpu().numpy(), f["o"], "max sizes")
+    assert np.abs(L.t["lse"].cpu().numpy() - f["lse"]).max() <= 2e-3
+    _log("max sizes: fine mass")
+    mp0 = L.t["mass_pool"].clone(); mw0 = L.t["mass_win"].clone()
+    L.fine_mass()
+    torch.cuda.synchronize()
+    ref = po.fine_mass(st, gsel, gcnt, scale, shape.T)
+    for n in ("mass_pool", "mass_win"):
+        got = L.t[n].cpu().numpy(); rr = ref[n]
+        assert np.abs(got - rr).max() <= 5e-3 * np.abs(rr).max() + 1e-7, n
+    _log("max sizes: update")
+    L.t["mass_pool"].copy_(mp0); L.t["mass_win"].copy_(mw0)
+    leaving = list(range(1024))
+    mp = mp0.cpu().numpy(); mw = mw0.cpu().numpy()
+    L.update(torch.tensor(leaving, dtype=torch.int32, device="cuda"), n_sink=0)
+    torch.cuda.synchronize()
+    u = po.memory_update(st, mp, mw, leaving, 0)
+    np.testing.assert_array_equal(L.t["pool_count"].cpu().numpy(), u["pool_count"])
+    n = int(u["pool_count"][0, 0])
+    np.testing.assert_array_equal(L.t["pool_id"][0, 0, :n].cpu().numpy(), u["pool_id"][0, 0, :n])
+    assert L.status_bits() == 0
