@@ -47,4 +47,16 @@ __device__ __forceinline__ bool ranks_before(float sa, int64_t ida, float sb, in
   return ida < idb;
 }
 
+// A 32-bit key whose unsigned order is that of ranks_before on the scores:
+// larger score -> larger key, -0 == +0, every NaN -> 1 (after all numbers,
+// whose keys are >= 0x007fffff).  Key 0 is left for slots that take no part.
+// With it, "a ranks before b" is ka > kb || (ka == kb && ida < idb), which
+// compiles to compares and masks with no branches.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (f != f) return 1u;
+  if ((u & 0x7fffffffu) == 0) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 }  // namespace pbsa

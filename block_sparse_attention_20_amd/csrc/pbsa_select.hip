@@ -102,8 +102,11 @@ __global__ __launch_bounds__(256) void slot_means_kernel(const TIn *__restrict__
 //  - top-k is rank based: a valid window slot is selected iff fewer than k
 //    valid slots rank before it in the total order (score desc, id asc, NaN
 //    last); its output position is the number of selected slots below it.
-//    Exact and order-independent, hence deterministic.
-// Dynamic LDS: q[128] floats, window ids [W] int64, s[C+W] floats, flags[W].
+//    Exact and order-independent, hence deterministic.  Scores enter the
+//    ranking as order keys (order_key; 0 = invalid slot), so the pairwise
+//    comparisons are branch free.
+// Dynamic LDS: q[128] floats, window ids [W] int64, keys [W], flags [W],
+// ranks [W].
 // ---------------------------------------------------------------------------
 constexpr int kScorePasses = 8;  // 16 candidates per pass
 
@@ -117,8 +120,8 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
   extern __shared__ __attribute__((aligned(16))) float smem[];
   float *qv = smem;                                        // [128]
   int64_t *wid = reinterpret_cast<int64_t *>(qv + 128);   // [W]
-  float *s = reinterpret_cast<float *>(wid + W);          // [C + W]
-  int *flag = reinterpret_cast<int *>(s + C + W);         // [W]: 1 valid, 2 selected
+  uint32_t *key = reinterpret_cast<uint32_t *>(wid + W);  // [W]: order keys
+  int *flag = reinterpret_cast<int *>(key + W);           // [W]: 1 valid, 2 selected
   int *rank = flag + W;                                    // [W]
   __shared__ int nvalid_sh;
   __shared__ int wcnt[4];
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
       if (sl == 0 && j < nj) {
         const float v = ok[ps] ? acc * scale : -INFINITY;
         srow[j] = v;
-        if (j < C + W) s[j] = v;
+        if (j >= C && j < C + W) key[j - C] = ok[ps] ? order_key(v) : 0u;
       }
     }
   }
@@ -203,14 +206,17 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
   {
     const int vq = (W + 3) / 4, v0 = wave * vq, v1 = min(W, v0 + vq);
     for (int w = lane; w < W; w += 64) {
-      if (!(flag[w] & 1)) continue;
-      const float sw = s[C + w];
+      const uint32_t kw = key[w];
       const int64_t iw = wid[w];
       int r = 0;
-#pragma unroll 4
-      for (int v = v0; v < v1; ++v)
-        r += (flag[v] & 1) && v != w && ranks_before(s[C + v], wid[v], sw, iw);
-      if (r) atomicAdd(&rank[w], r);
+      // an invalid v has key 0 and never ranks before a valid w; v == w
+      // fails both terms
+#pragma unroll 8
+      for (int v = v0; v < v1; ++v) {
+        const uint32_t kv = key[v];
+        r += (int)((kv > kw) | ((kv == kw) & (wid[v] < iw)));
+      }
+      if (r && kw != 0) atomicAdd(&rank[w], r);
     }
   }
   __syncthreads();
@@ -347,7 +353,7 @@ size_t select_ws_bytes(const pbsa_problem &p) {
 }
 
 size_t select_lds_bytes(const pbsa_problem &p) {
-  return (128 + (size_t)p.C + p.W) * sizeof(float) + (size_t)p.W * (2 * sizeof(int) + sizeof(int64_t));
+  return 128 * sizeof(float) + (size_t)p.W * (sizeof(uint32_t) + 2 * sizeof(int) + sizeof(int64_t));
 }
 
 hipError_t launch_select(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,

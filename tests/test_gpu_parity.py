@@ -252,6 +252,74 @@ def test_block_mass_later_equals_mass_in_select():
     assert torch.equal(L.t["mass_pool"], ref["mass_pool"]) and torch.equal(L.t["mass_win"], ref["mass_win"])
 
 
+def _topk_from_scores(srow_win, valid, ids, k):
+    """Window slots of the k best valid scores under the total order (score
+    descending, ties by id ascending, NaN after every number), ascending."""
+    cand = [w for w in range(len(valid)) if valid[w]]
+    cand.sort(key=lambda w: (bool(np.isnan(srow_win[w])),
+                             0.0 if np.isnan(srow_win[w]) else -float(srow_win[w]), int(ids[w])))
+    return sorted(cand[:min(k, len(cand))])
+
+
+@pytest.mark.parametrize("k", [2, 5, 7, 36])
+def test_topk_exact_on_kernel_scores(k):
+    """The selection equals the top-k of the kernel's own fp32 coarse scores
+    (read back from the select workspace), bit for bit, with exact ties:
+    groups of window slots hold identical keys (so identical scores) and
+    their ids are not in slot order, so only the id decides among them; two
+    valid slots hold NaN keys and must rank after every number (k = 36 of 37
+    valid slots leaves out exactly the NaN slot of the larger id); empty
+    slots never count."""
+    W, C, T, d = 40, 3, 64, 64
+    shape = syn.Shape(B=1, H=2, d=d, T=T, Nq=3 * T - 9, W=W, C=C, topk=k)
+    win_len = [T] * W
+    for w in (3, 14, 27):
+        win_len[w] = 0
+    win_len[33] = 20
+    rng = np.random.default_rng(5)
+    ids = [int(x) for x in 100 + rng.permutation(W)]
+    st = syn.make_state(shape, 29, sigma=1.0, shift=1.0, win_len=win_len, win_id=ids, pool_count=[3, 2])
+    kw = st["k_win"].float()
+    qm = st["q"].float().mean(dim=2)  # [B,H,d]: the queries' common direction
+    top, second, nan_slots = (2, 9, 17, 30), (5, 22, 36), (11, 25)
+    for w in top:
+        kw[:, :, w, :] = 4.0 * qm[:, :, None, :]
+    for w in second:
+        kw[:, :, w, :] = 2.0 * qm[:, :, None, :]
+    for w in nan_slots:
+        kw[:, :, w, :] = float("nan")
+    st["k_win"] = kw.to(shape.dtype)
+    _log(f"top-k exact on kernel scores: k={k}")
+    L = PBSALayer(shape.B, shape.H, shape.d, shape.T, shape.Nq, shape.W, shape.C, shape.topk,
+                  dtype=shape.dtype, device="cuda").load(st)
+    L.select(masses=False)
+    torch.cuda.synchronize()
+    QB = (shape.Nq + T - 1) // T
+    bh = shape.B * shape.H
+    off = (bh * QB * d * 4 + 255) // 256 * 256
+    nj = C + W + QB
+    srows = L.ws_select[off:off + bh * QB * nj * 4].view(torch.float32).cpu().numpy().reshape(bh, QB, nj)
+    sel = L.t["sel"].cpu().numpy().reshape(bh, QB, k)
+    cnt = L.t["sel_count"].cpu().numpy().reshape(bh, QB)
+    valid = [x > 0 for x in win_len]
+    n_valid = sum(valid)
+    for b in range(bh):
+        for i in range(QB):
+            sw = srows[b, i, C:C + W]
+            assert np.isnan(sw[list(nan_slots)]).all()
+            assert len(set(float(sw[w]) for w in top)) == 1
+            exp = _topk_from_scores(sw, valid, ids, k)
+            assert int(cnt[b, i]) == min(k, n_valid)
+            got = [int(x) for x in sel[b, i, :cnt[b, i]]]
+            assert got == exp, (b, i, got, exp)
+            assert (sel[b, i, cnt[b, i]:] == -1).all()
+    if k == 2:
+        # the top group is ahead of everything else in every row, so the two
+        # smallest ids of the group are the selection
+        want = sorted(sorted(top, key=lambda w: ids[w])[:2])
+        assert all([int(x) for x in sel[b, i, :2]] == want for b in range(bh) for i in range(QB))
+
+
 def test_fwd_deterministic_and_fully_written():
     shape, kw = CASES["bf16_d64_T64_multi"]
     st = syn.make_state(shape, 3, **kw)
