@@ -108,7 +108,11 @@ __global__ __launch_bounds__(256) void slot_means_kernel(const TIn *__restrict__
 // Dynamic LDS: q[128] floats, window ids [W] int64, keys [W], flags [W],
 // ranks [W].
 // ---------------------------------------------------------------------------
-constexpr int kScorePasses = 8;  // 16 candidates per pass
+// 16 candidates per pass; 9 passes cover the 143 candidates of the Wan
+// chunk (pool 32 + window 74 + 37 current blocks) with one batch of loads:
+// 16.3 us for means + scores + top-k there, against 18.6 us with 8 (which
+// needs a second, almost empty batch) and 16.5 us with 3 or 5.
+constexpr int kScorePasses = 9;
 
 __global__ __launch_bounds__(256) void score_topk_kernel(
     const float *__restrict__ qbar, const float *__restrict__ kbar_pool,
