@@ -86,6 +86,17 @@ __device__ __forceinline__ int split_owner(const FwdArgs &a, int64_t u) {
   return (int)(((u + 1) * a.G - 1) / a.U);
 }
 
+// Partial results of split items travel through the device-coherent level:
+// 16- and 8-byte buffer accesses with the device-scope cache policy (sc1),
+// the stores completed (vmcnt 0) before the arrival is counted.  An
+// agent-scope fence would instead write back and invalidate the XCD's whole
+// L2 (buffer_wbl2 / buffer_inv sc1) and throw away the K/V lines that the
+// other workgroups on that XCD are streaming.
+constexpr int kScDevice = 16;  // buffer cache-policy bit sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const float *p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, 0x7fffffff, 0x00020000);
+}
+
 // Arrival on an epoch-tagged counter (high word: launch epoch, low word:
 // arrivals in that launch); returns the arrivals including this one.  A
 // word with another epoch (garbage, or an earlier launch) counts as zero, and
@@ -353,24 +364,33 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
   float l = (l4[0] + l4[1]) + (l4[2] + l4[3]);
   l += __shfl_xor(l, 32);
   if (j0 > 0 || j1 < a.NB) {
-    // piece of a split item: publish it, and merge if it is the last one
+    // piece of a split item: publish it, and merge if it is the last one.
+    // The pieces are those of workgroups ga..gb (slot 2 g for a workgroup's
+    // first item, 2 g + 1 for its second); the merge reads every piece back
+    // (its own too) in that order whichever arrives last, so the result
+    // does not depend on the arrival order.
     const int64_t first_u = (int64_t)item * a.NB;
-    const int slot = 2 * wg + (split_start(a, wg) / a.NB == item ? 0 : 1);
+    const int ga = split_owner(a, first_u), gb = split_owner(a, first_u + a.NB - 1);
+    const int own = wg;
+    auto slot_of = [&](int gg) -> uint32_t {
+      return 2 * gg + (split_start(a, gg) / a.NB == item ? 0 : 1);
+    };
+    const __amdgpu_buffer_rsrc_t ro = part_rsrc(a.part_o), rml = part_rsrc(a.part_ml);
     {
-      float *po = a.part_o + ((size_t)slot * (2 * BT) + t) * (D / 2);
+      const uint32_t ob = ((slot_of(own) * (2 * BT) + t) * (D / 2)) * 4;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4)
-          *reinterpret_cast<f32x4 *>(po + dt * 16 + 4 * e4) =
-              f32x4{oacc[dt][4 * e4], oacc[dt][4 * e4 + 1], oacc[dt][4 * e4 + 2], oacc[dt][4 * e4 + 3]};
-      float *pm = a.part_ml + ((size_t)slot * (2 * BT) + t) * 2;
-      pm[0] = m;
-      pm[1] = l;
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const u32x4 v = {__float_as_uint(oacc[dt][4 * e4]), __float_as_uint(oacc[dt][4 * e4 + 1]),
+                           __float_as_uint(oacc[dt][4 * e4 + 2]), __float_as_uint(oacc[dt][4 * e4 + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(v, ro, ob + (dt * 16 + 4 * e4) * 4, 0, kScDevice);
+        }
+      const u32x2 ml = {__float_as_uint(m), __float_as_uint(l)};
+      __builtin_amdgcn_raw_buffer_store_b64(ml, rml, (slot_of(own) * (2 * BT) + t) * 8, 0, kScDevice);
     }
-    __threadfence();
-    __syncthreads();
-    const int ga = split_owner(a, first_u), gb = split_owner(a, first_u + a.NB - 1);
+    PBSA_WAIT_VM(0);  // this thread's partial has reached the device-coherent level
+    __syncthreads();  // ... and every thread's
     if (t == 0) {
       sh.last = arrive(a.cnt + item, a.epoch) == gb - ga + 1;
       // every piece of this launch has arrived: leave the counter at zero
@@ -378,7 +398,6 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
     }
     __syncthreads();
     if (!sh.last) return;
-    __threadfence();
     float M = -INFINITY, L = 0.f;
     f32x16 acc[D / 32];
 #pragma unroll
@@ -386,20 +405,20 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
     for (int gg = ga; gg <= gb; ++gg) {
-      const int sl = 2 * gg + (split_start(a, gg) / a.NB == item ? 0 : 1);
-      const float *po = a.part_o + ((size_t)sl * (2 * BT) + t) * (D / 2);
-      const float *pm = a.part_ml + ((size_t)sl * (2 * BT) + t) * 2;
-      const float mg = pm[0], lg = pm[1];
+      const uint32_t sl = slot_of(gg);
+      const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(rml, (sl * (2 * BT) + t) * 8, 0, kScDevice);
+      const float mg = __uint_as_float(ml[0]), lg = __uint_as_float(ml[1]);
       if (mg == -INFINITY) continue;
       const float mn = fmaxf(M, mg);
       const float ca = __builtin_amdgcn_exp2f(M - mn), cb = __builtin_amdgcn_exp2f(mg - mn);
+      const uint32_t ob = ((sl * (2 * BT) + t) * (D / 2)) * 4;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-          const f32x4 v = *reinterpret_cast<const f32x4 *>(po + dt * 16 + 4 * e4);
+          const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(ro, ob + (dt * 16 + 4 * e4) * 4, 0, kScDevice);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) acc[dt][4 * e4 + k] = acc[dt][4 * e4 + k] * ca + v[k] * cb;
+          for (int k = 0; k < 4; ++k) acc[dt][4 * e4 + k] = acc[dt][4 * e4 + k] * ca + __uint_as_float(w[k]) * cb;
         }
       L = L * ca + lg * cb;
       M = mn;
