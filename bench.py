@@ -40,9 +40,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # FETCH 14,167 KiB, WRITE 28,304 KiB).  Valid only for the kernel source it
 # was measured on (sha1 over FWD_SOURCES below); reported as null once those
 # sources change.
-FWD_TRAFFIC = {"src_sha1": "cee553ba2d23046dd1f06a788f1acde8a93f5939",
-               "fetch_kib": 60229.9, "write_kib": 14259.9,
-               "fetch_scale": 28302.0 / 14166.7, "write_scale": 28302.0 / 28304.3}
+FWD_TRAFFIC = {"src_sha1": "a6846eb92911b0d316b162f82b2f1c2ded1016c0",
+               "fetch_kib": 60350.3, "write_kib": 14260.0,
+               "fetch_scale": 28302.0 / 14166.6, "write_scale": 28302.0 / 28304.3}
 
 
 FWD_SOURCES = ("pbsa_attn_fwd.hip", "pbsa_tiles.h")
