@@ -553,16 +553,20 @@ __global__ __launch_bounds__(2 * BT) void attn_fwd_f32_kernel(FwdArgs a) {
 constexpr int kSplitSlots = 512;
 
 static int split_slots() {
-  static int cached[64];
+  // per device, filled on first use; concurrent first calls store the same
+  // value, and the atomics keep that free of data races
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kSplitSlots;
-  if (cached[dev] == 0) {
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = kSplitSlots / 2;
-    cached[dev] = 2 * n < kSplitSlots ? 2 * n : kSplitSlots;
+    v = 2 * n < kSplitSlots ? 2 * n : kSplitSlots;
+    cached[dev].store(v, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return v;
 }
 
 static size_t split_part_o_bytes(const pbsa_problem &p) {
