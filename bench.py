@@ -314,6 +314,81 @@ def sweep(torch, device="cuda", reps=3, iters=10):
     return out
 
 
+def small_chunks(torch, device="cuda", iters=20):
+    """Forward on short query chunks, where the kernel is bound by memory:
+    1-8 query blocks of the Wan head shape (12 heads x 128, blocks of 128)
+    against the full-size cache (window 74 slots, pool 32, top-16), and the
+    tiny fp32 configuration.  Algorithmic bytes per launch: Q and O, LSE,
+    and the valid rows of K and V of every block attended (pool, the union
+    of the selected window blocks over the query blocks, the current chunk),
+    each moved once.  Cold: L2 and Infinity Cache flushed (a 512 MB write)
+    before each timed launch; warm: back-to-back launches."""
+    import statistics
+
+    import pbsa_synth as syn
+    from block_sparse_attention_20_amd.layer import PBSALayer
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=device)
+    base = syn.WAN_CHUNK
+    cases = [(f"{qb} query block{'s' if qb > 1 else ''} x 12 heads, Wan cache",
+              syn.Shape(B=1, H=base.H, d=base.d, T=base.T, Nq=qb * base.T, W=base.W, C=base.C,
+                        topk=base.topk)) for qb in (1, 2, 4, 8)]
+    cases.append(("tiny fp32 (1 head x 64, 256 tokens, window 32, pool 4, top-4)", syn.TINY_F32))
+    out = []
+    for name, shape in cases:
+        log(f"small chunks: {name}")
+        if shape.dtype == torch.float32:
+            st = syn.tiny_f32_state(device=device)
+        else:
+            st = syn.make_state(shape, 6000 + shape.Nq // shape.T, sigma=1 / math.sqrt(shape.d), shift=1.5,
+                                n_planted=8, win_len=syn.chunk_window_lens(base.Nq, base.T, 2),
+                                device=device)
+        L = PBSALayer(shape.B, shape.H, shape.d, shape.T, shape.Nq, shape.W, shape.C, shape.topk,
+                      dtype=shape.dtype, device=device).load(st)
+        del st
+        L.select()
+        L.fwd()
+        torch.cuda.synchronize()
+        esz = 2 if shape.dtype == torch.bfloat16 else 4
+        row_b = shape.d * esz
+        t = {k: L.t[k].cpu() for k in ("pool_count", "pool_len", "sel", "sel_count", "win_len")}
+        alg = 0
+        for b in range(shape.B):
+            for h in range(shape.H):
+                n_pool = int(t["pool_count"][b, h])
+                kv = sum(int(x) for x in t["pool_len"][b, h, :n_pool])
+                used = set()
+                for i in range(L.QB):
+                    used.update(int(w) for w in t["sel"][b, h, i, :int(t["sel_count"][b, h, i])])
+                kv += sum(int(t["win_len"][w]) for w in used) + shape.Nq
+                alg += 2 * kv * row_b + 2 * shape.Nq * row_b + 4 * shape.Nq
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for r in range(iters):
+            flush.fill_(r & 255)
+            ev[r][0].record()
+            L.fwd()
+            ev[r][1].record()
+        torch.cuda.synchronize()
+        cold = statistics.median(a.elapsed_time(b) * 1e3 for a, b in ev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            L.fwd()
+        b.record()
+        torch.cuda.synchronize()
+        warm = a.elapsed_time(b) * 1e3 / iters
+        out.append({"case": name, "query_blocks": L.QB, "items": shape.B * shape.H * L.QB,
+                    "dtype": "bf16" if esz == 2 else "f32", "alg_mb": round(alg / 1e6, 2),
+                    "cold_us": round(cold, 1), "warm_us": round(warm, 1),
+                    "cold_gbs": round(alg / (cold * 1e-6) / 1e9, 1),
+                    "warm_gbs": round(alg / (warm * 1e-6) / 1e9, 1),
+                    "cold_frac_of_8tbs": round(alg / (cold * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)})
+        del L
+        torch.cuda.empty_cache()
+    del flush
+    return {"workload": "forward on short query chunks against the Wan-sized cache, and the tiny "
+                        "fp32 configuration (memory-bound sizes)", "rows": out}
+
+
 def mass_compare(torch, n_chunks=16, n_layers=2, device="cuda"):
     """Coarse vs exact (fine-grained) block mass as the Top-C score, and the
     head-shared pool (one pool per layer, coarse masses summed over heads), on the
@@ -500,6 +575,8 @@ def main():
                     help="only the sparsity x history sweep of the forward (its own JSON line)")
     ap.add_argument("--train-rollout", action="store_true",
                     help="only the training-through-a-rollout timing (its own JSON line)")
+    ap.add_argument("--small-chunks", action="store_true",
+                    help="forward on 1-8 query blocks and the tiny fp32 case: HBM GB/s")
     ap.add_argument("--mass-compare", action="store_true",
                     help="only the coarse vs exact block-mass comparison (its own JSON line)")
     args = ap.parse_args()
@@ -518,6 +595,9 @@ def main():
         return
     if args.train_rollout:
         print(json.dumps({"train_rollout": train_rollout_bench(torch, device=dev)}), flush=True)
+        return
+    if args.small_chunks:
+        print(json.dumps({"small_chunks": small_chunks(torch, device=dev)}), flush=True)
         return
     if args.mass_compare:
         print(json.dumps({"mass_compare": mass_compare(torch, device=dev)}), flush=True)

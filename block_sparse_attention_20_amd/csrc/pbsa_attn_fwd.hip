@@ -551,6 +551,12 @@ __global__ __launch_bounds__(2 * BT) void attn_fwd_f32_kernel(FwdArgs a) {
 // Resident workgroups of the split launch: two per CU (LDS and VGPR
 // budget of the bf16 kernel), at most kSplitSlots.
 constexpr int kSplitSlots = 512;
+// Pieces per query block in the split launch.  The merge reads every
+// piece's partial back one piece after another, so few long pieces beat
+// many short ones: forward on 1-4 query blocks x 12 heads of the Wan
+// cache took 74-81 us (cold caches) with 4, 79-84 with 3, 92-95 with 2,
+// and 186-387 us uncapped (up to 43 pieces per block).
+constexpr int kMaxPieces = 4;
 
 static int split_slots() {
   // per device, filled on first use; concurrent first calls store the same
@@ -616,7 +622,9 @@ hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, co
   if (p.dtype == PBSA_BF16 && ws != nullptr && ws_bytes >= fwd_ws_bytes(p) &&
       2 * (int64_t)a.n_items <= slots) {
     a.split = 1;
-    a.G = (int)(a.U < slots ? a.U : slots);
+    const int64_t cap = (int64_t)a.n_items * kMaxPieces;
+    const int64_t g = a.U < slots ? a.U : slots;
+    a.G = (int)(g < cap ? g : cap);
     uint32_t e = ++epoch_counter;
     if (e == 0) e = ++epoch_counter;
     a.epoch = e;
