@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # FETCH 14,167 KiB, WRITE 28,304 KiB).  Valid only for the kernel source it
 # was measured on (sha1 over FWD_SOURCES below); reported as null once those
 # sources change.
-FWD_TRAFFIC = {"src_sha1": "7ad39c743393db109c48ad8c8b20fe358ff85ea5",
+FWD_TRAFFIC = {"src_sha1": "657dc4c9b7fa160ca376202923c6fc38f381a7ff",
                "fetch_kib": 60350.3, "write_kib": 14260.0,
                "fetch_scale": 28302.0 / 14166.6, "write_scale": 28302.0 / 28304.3}
 
