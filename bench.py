@@ -40,8 +40,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # FETCH 14,167 KiB, WRITE 28,304 KiB).  Valid only for the kernel source it
 # was measured on (sha1 over FWD_SOURCES below); reported as null once those
 # sources change.
-FWD_TRAFFIC = {"src_sha1": "657dc4c9b7fa160ca376202923c6fc38f381a7ff",
-               "fetch_kib": 60350.3, "write_kib": 14260.0,
+FWD_TRAFFIC = {"src_sha1": "14994e1ca4dad29a3436e61d471f8475b963eb4d",
+               "fetch_kib": 59807.1, "write_kib": 14259.9,
                "fetch_scale": 28302.0 / 14166.6, "write_scale": 28302.0 / 28304.3}
 
 

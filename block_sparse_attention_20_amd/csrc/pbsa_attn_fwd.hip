@@ -31,14 +31,17 @@
 //     ds_read_b64_tr_b16 (two 4x16 transposed reads per fragment); this part
 //     runs at raised wave priority;
 //   - work items are mapped XCD-aware: consecutive query blocks of a head
-//     run on the same XCD and share its L2 for the pool/current K/V.
-// fp32 path: plain vector FMA version of the same walk (small problems).
+//     run on the same XCD and share its L2 for the pool/current K/V;
+//   - with a workspace and at most half the resident slots' worth of query
+//     blocks, the list visits are split evenly over up to 8 workgroups per
+//     query block; each piece writes a partial and attn_fwd_merge_kernel
+//     combines them after the launch, in a fixed order.
+// fp32 path: vector FMA version of the same walk (small problems).
 #include "pbsa_common.h"
 #include "pbsa_internal.h"
 #include "pbsa_tiles.h"
 
 #include <atomic>
-#include <chrono>
 #include <type_traits>
 
 namespace pbsa {
@@ -51,16 +54,13 @@ struct FwdArgs {
   int32_t *status;
   int H, Nq, W, C, topk, QB, n_items, per_xcd;
   float sl2;  // scale * log2(e)
-  // balanced split (see split_range): NB list entries per item, G
-  // workgroups sharing U = n_items * NB block visits; partial results of
-  // items cut between workgroups go to part_o / part_ml and are merged by
-  // the last workgroup to finish its piece (cnt: arrival counters tagged
-  // with this launch's epoch).
+  // balanced split: NB list entries per item, G workgroups sharing
+  // U = n_items * NB block visits; partial results of items cut between
+  // workgroups go to part_o / part_ml, and attn_fwd_merge_kernel combines
+  // them after the forward launch.
   int split, NB, G;
-  uint32_t epoch;
   int64_t U;
   float *part_o, *part_ml;
-  unsigned long long *cnt;
 };
 
 __device__ __forceinline__ void item_of_block(const FwdArgs &a, int &item) {
@@ -86,42 +86,14 @@ __device__ __forceinline__ int split_owner(const FwdArgs &a, int64_t u) {
   return (int)(((u + 1) * a.G - 1) / a.U);
 }
 
-// Partial results of split items travel through the device-coherent level:
-// 16- and 8-byte buffer accesses with the device-scope cache policy (sc1),
-// the stores completed (vmcnt 0) before the arrival is counted.  An
-// agent-scope fence would instead write back and invalidate the XCD's whole
-// L2 (buffer_wbl2 / buffer_inv sc1) and throw away the K/V lines that the
-// other workgroups on that XCD are streaming.
-constexpr int kScDevice = 16;  // buffer cache-policy bit sc1
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const float *p) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, 0x7fffffff, 0x00020000);
-}
-
-// Arrival on an epoch-tagged counter (high word: launch epoch, low word:
-// arrivals in that launch); returns the arrivals including this one.  A
-// word with another epoch (garbage, or an earlier launch) counts as zero, and
-// the last arrival of a launch resets it to zero.
-__device__ __forceinline__ int arrive(unsigned long long *c, uint32_t epoch) {
-  unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  while (true) {
-    const unsigned long long nv =
-        (uint32_t)(old >> 32) == epoch ? old + 1 : (((unsigned long long)epoch << 32) | 1ull);
-    const unsigned long long prev = atomicCAS(c, old, nv);
-    if (prev == old) return (int)(uint32_t)nv;
-    old = prev;
-  }
-}
-
 template <int D, int BT>
 struct FwdLds {
   BlockList blist;
-  int last;
 };
 
 // Entries [j0, j1) of item `item`'s block list.  A whole item (0, NB)
 // writes O and LSE; a piece writes its unnormalised O^T, running max and row
-// sum to its partial slot, and the last piece to arrive merges all pieces of
-// the item in workgroup order (so the result does not depend on timing).
+// sum to its partial slot for attn_fwd_merge_kernel.
 // max of x over lanes l and l ^ 32 (v_permlane32_swap exchanges the two
 // lane halves of a register; no LDS round trip)
 __device__ __forceinline__ float half_swap_max(float x) {
@@ -364,69 +336,22 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
   float l = (l4[0] + l4[1]) + (l4[2] + l4[3]);
   l += __shfl_xor(l, 32);
   if (j0 > 0 || j1 < a.NB) {
-    // piece of a split item: publish it, and merge if it is the last one.
-    // The pieces are those of workgroups ga..gb (slot 2 g for a workgroup's
-    // first item, 2 g + 1 for its second); the merge reads every piece back
-    // (its own too) in that order whichever arrives last, so the result
-    // does not depend on the arrival order.
-    const int64_t first_u = (int64_t)item * a.NB;
-    const int ga = split_owner(a, first_u), gb = split_owner(a, first_u + a.NB - 1);
-    const int own = wg;
-    auto slot_of = [&](int gg) -> uint32_t {
-      return 2 * gg + (split_start(a, gg) / a.NB == item ? 0 : 1);
-    };
-    const __amdgpu_buffer_rsrc_t ro = part_rsrc(a.part_o), rml = part_rsrc(a.part_ml);
-    {
-      const uint32_t ob = ((slot_of(own) * (2 * BT) + t) * (D / 2)) * 4;
+    // piece of a split item: its partial goes to slot 2 wg (the workgroup's
+    // first item) or 2 wg + 1 (its second), laid out [slot][dt][thread][16]
+    // so that the merge of one dt reads a contiguous 16 KB
+    const int slot = 2 * wg + (split_start(a, wg) / a.NB == item ? 0 : 1);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt) {
+      float *po = a.part_o + (((size_t)slot * (D / 32) + dt) * (2 * BT) + t) * 16;
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const u32x4 v = {__float_as_uint(oacc[dt][4 * e4]), __float_as_uint(oacc[dt][4 * e4 + 1]),
-                           __float_as_uint(oacc[dt][4 * e4 + 2]), __float_as_uint(oacc[dt][4 * e4 + 3])};
-          __builtin_amdgcn_raw_buffer_store_b128(v, ro, ob + (dt * 16 + 4 * e4) * 4, 0, kScDevice);
-        }
-      const u32x2 ml = {__float_as_uint(m), __float_as_uint(l)};
-      __builtin_amdgcn_raw_buffer_store_b64(ml, rml, (slot_of(own) * (2 * BT) + t) * 8, 0, kScDevice);
+      for (int e4 = 0; e4 < 4; ++e4)
+        *reinterpret_cast<f32x4 *>(po + 4 * e4) =
+            f32x4{oacc[dt][4 * e4], oacc[dt][4 * e4 + 1], oacc[dt][4 * e4 + 2], oacc[dt][4 * e4 + 3]};
     }
-    PBSA_WAIT_VM(0);  // this thread's partial has reached the device-coherent level
-    __syncthreads();  // ... and every thread's
-    if (t == 0) {
-      sh.last = arrive(a.cnt + item, a.epoch) == gb - ga + 1;
-      // every piece of this launch has arrived: leave the counter at zero
-      if (sh.last) __hip_atomic_store(a.cnt + item, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!sh.last) return;
-    float M = -INFINITY, L = 0.f;
-    f32x16 acc[D / 32];
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
-    for (int gg = ga; gg <= gb; ++gg) {
-      const uint32_t sl = slot_of(gg);
-      const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(rml, (sl * (2 * BT) + t) * 8, 0, kScDevice);
-      const float mg = __uint_as_float(ml[0]), lg = __uint_as_float(ml[1]);
-      if (mg == -INFINITY) continue;
-      const float mn = fmaxf(M, mg);
-      const float ca = __builtin_amdgcn_exp2f(M - mn), cb = __builtin_amdgcn_exp2f(mg - mn);
-      const uint32_t ob = ((sl * (2 * BT) + t) * (D / 2)) * 4;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(ro, ob + (dt * 16 + 4 * e4) * 4, 0, kScDevice);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) acc[dt][4 * e4 + k] = acc[dt][4 * e4 + k] * ca + __uint_as_float(w[k]) * cb;
-        }
-      L = L * ca + lg * cb;
-      M = mn;
-    }
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = acc[dt];
-    m = M;
-    l = L;
+    float *pm = a.part_ml + ((size_t)slot * (2 * BT) + t) * 2;
+    pm[0] = m;
+    pm[1] = l;
+    return;
   }
   // O = O^T / l, LSE = ln(sum exp(scale s))
   const float inv = 1.f / l;
@@ -464,6 +389,61 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kerne
     const int j1 = (int)(u1 - base < a.NB ? u1 - base : a.NB);
     fwd_segment<D, BT>(a, sh, K0, K1, V0, V1, wg, item, j0, j1);
   }
+}
+
+// Merge of the split pieces, one workgroup per (query block, 32 of the d
+// output columns); thread t holds the same rows and columns as thread t of
+// the forward.  Two passes over the pieces in workgroup order: the max M of
+// their running maxima, then O = sum_g 2^(m_g - M) O_g / sum_g 2^(m_g - M) l_g.
+// The order is fixed, so the result does not depend on timing; the kernel
+// boundary orders the pieces' stores before these loads.  Query blocks that
+// one workgroup covered whole were written by the forward and are skipped.
+template <int D, int BT>
+__global__ __launch_bounds__(2 * BT) void attn_fwd_merge_kernel(FwdArgs a) {
+  const int item = blockIdx.x / (D / 32), dt = blockIdx.x % (D / 32);
+  if (item >= a.n_items) return;
+  const int64_t first_u = (int64_t)item * a.NB;
+  const int ga = split_owner(a, first_u), gb = split_owner(a, first_u + a.NB - 1);
+  if (ga == gb) return;
+  const int i = item % a.QB;
+  const size_t bh = item / a.QB;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int qrow = i * BT + wave * 32 + l32;
+  auto slot_of = [&](int gg) -> size_t {
+    return 2 * (size_t)gg + (split_start(a, gg) / a.NB == item ? 0 : 1);
+  };
+  float M = -INFINITY;
+  for (int gg = ga; gg <= gb; ++gg) M = fmaxf(M, a.part_ml[(slot_of(gg) * (2 * BT) + t) * 2]);
+  float L = 0.f;
+  float acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll 2
+  for (int gg = ga; gg <= gb; ++gg) {
+    const size_t sl = slot_of(gg);
+    const float mg = a.part_ml[(sl * (2 * BT) + t) * 2], lg = a.part_ml[(sl * (2 * BT) + t) * 2 + 1];
+    const float w = mg == -INFINITY ? 0.f : exp2f(mg - M);
+    L += w * lg;
+    const float *po = a.part_o + ((sl * (D / 32) + dt) * (2 * BT) + t) * 16;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(po + 4 * e4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[4 * e4 + k] += w * v[k];
+    }
+  }
+  if (qrow >= a.Nq) return;
+  const float inv = 1.f / L;
+  uint16_t *op = (uint16_t *)a.o + (bh * a.Nq + qrow) * (size_t)D;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    u32x2 pk;
+    pk[0] = pack_bf16x2(acc[4 * jj] * inv, acc[4 * jj + 1] * inv);
+    pk[1] = pack_bf16x2(acc[4 * jj + 2] * inv, acc[4 * jj + 3] * inv);
+    *reinterpret_cast<u32x2 *>(op + dt * 32 + 8 * jj + 4 * g) = pk;
+  }
+  if (dt == 0 && g == 0 && a.lse) a.lse[bh * a.Nq + qrow] = (M + log2f(L)) * kLn2;
 }
 
 // fp32 vector path: kF32Tpr threads per query row, each owning D / kF32Tpr
@@ -559,12 +539,11 @@ __global__ __launch_bounds__(kF32Tpr * BT) void attn_fwd_f32_kernel(FwdArgs a) {
 // Resident workgroups of the split launch: two per CU (LDS and VGPR
 // budget of the bf16 kernel), at most kSplitSlots.
 constexpr int kSplitSlots = 512;
-// Pieces per query block in the split launch.  The merge reads every
-// piece's partial back one piece after another, so few long pieces beat
-// many short ones: forward on 1-4 query blocks x 12 heads of the Wan
-// cache took 74-81 us (cold caches) with 4, 79-84 with 3, 92-95 with 2,
-// and 186-387 us uncapped (up to 43 pieces per block).
-constexpr int kMaxPieces = 4;
+// Pieces per query block in the split launch.  More pieces keep more
+// loads in flight but each adds a partial to write and merge: forward on
+// 1-4 query blocks x 12 heads of the Wan cache took 47-55 us (cold
+// caches) with 8, 57-58 with 4, 50-70 with 16, 63-69 with 32.
+constexpr int kMaxPieces = 8;
 
 static int split_slots() {
   // per device, filled on first use; concurrent first calls store the same
@@ -592,19 +571,12 @@ static size_t split_part_ml_bytes(const pbsa_problem &p) {
 
 size_t fwd_ws_bytes(const pbsa_problem &p) {
   if (p.dtype != PBSA_BF16) return 0;
-  const size_t n_items = (size_t)p.B * p.H * ((p.Nq + p.T - 1) / p.T);
-  return split_part_o_bytes(p) + split_part_ml_bytes(p) +
-         align256(n_items * sizeof(unsigned long long));
+  return split_part_o_bytes(p) + split_part_ml_bytes(p);
 }
 
 hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
                            const int32_t *sel, const int32_t *sel_count, void *o, float *lse,
                            void *ws, size_t ws_bytes, hipStream_t st) {
-  // launch epochs: consecutive from a start that differs between library
-  // instances, so a workspace handed over from another instance in the same
-  // process cannot match
-  static std::atomic<uint32_t> epoch_counter{
-      (uint32_t)((uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761ull)};
   FwdArgs a;
   a.q = q;
   a.k_cur = kv.k_cur; a.v_cur = kv.v_cur; a.k_win = kv.k_win; a.v_win = kv.v_win;
@@ -619,9 +591,7 @@ hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, co
   a.U = (int64_t)a.n_items * a.NB;
   a.split = 0;
   a.G = 0;
-  a.epoch = 0;
   a.part_o = a.part_ml = nullptr;
-  a.cnt = nullptr;
   int n_wg = a.n_items;
   const int64_t slots = split_slots();
   // The split pays off only when one workgroup per query block would leave
@@ -633,22 +603,20 @@ hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, co
     const int64_t cap = (int64_t)a.n_items * kMaxPieces;
     const int64_t g = a.U < slots ? a.U : slots;
     a.G = (int)(g < cap ? g : cap);
-    uint32_t e = ++epoch_counter;
-    if (e == 0) e = ++epoch_counter;
-    a.epoch = e;
     char *w = reinterpret_cast<char *>(ws);
     a.part_o = reinterpret_cast<float *>(w);
     a.part_ml = reinterpret_cast<float *>(w + split_part_o_bytes(p));
-    a.cnt = reinterpret_cast<unsigned long long *>(w + split_part_o_bytes(p) + split_part_ml_bytes(p));
     n_wg = a.G;
   }
   a.per_xcd = (n_wg + 7) / 8;
   const dim3 grid(8 * a.per_xcd);
   const dim3 block(2 * p.T);
-#define PBSA_FWD_CASE(DT, D_, T_, KERN)                         \
-  if (p.dtype == DT && p.d == D_ && p.T == T_) {                \
-    KERN<D_, T_><<<grid, block, 0, st>>>(a);                    \
-    return hipGetLastError();                                   \
+#define PBSA_FWD_CASE(DT, D_, T_, KERN)                                              \
+  if (p.dtype == DT && p.d == D_ && p.T == T_) {                                     \
+    KERN<D_, T_><<<grid, block, 0, st>>>(a);                                         \
+    if (a.split)                                                                     \
+      attn_fwd_merge_kernel<D_, T_><<<dim3(a.n_items * (D_ / 32)), block, 0, st>>>(a); \
+    return hipGetLastError();                                                        \
   }
   PBSA_FWD_CASE(PBSA_BF16, 128, 128, attn_fwd_bf16_kernel)
   PBSA_FWD_CASE(PBSA_BF16, 64, 128, attn_fwd_bf16_kernel)
