@@ -38,20 +38,14 @@ __device__ __forceinline__ void set_status(int32_t *st, int bit) {
   if (st) atomicOr(st, bit);
 }
 
-// Total order of the routing decisions: larger score first, then smaller id,
-// NaN after every number (NaNs among themselves by id).
-__device__ __forceinline__ bool ranks_before(float sa, int64_t ida, float sb, int64_t idb) {
-  bool na = sa != sa, nb = sb != sb;
-  if (na != nb) return nb;
-  if (!na && sa != sb) return sa > sb;
-  return ida < idb;
-}
-
-// A 32-bit key whose unsigned order is that of ranks_before on the scores:
-// larger score -> larger key, -0 == +0, every NaN -> 1 (after all numbers,
-// whose keys are >= 0x007fffff).  Key 0 is left for slots that take no part.
-// With it, "a ranks before b" is ka > kb || (ka == kb && ida < idb), which
-// compiles to compares and masks with no branches.
+// Total order of the routing decisions (top-k over window scores, Top-C
+// over block masses): larger value first, then smaller id, NaN after every
+// number (NaNs among themselves by id).  order_key maps a value to a 32-bit
+// key whose unsigned order is that order on the values: larger value ->
+// larger key, -0 == +0, every NaN -> 1 (below all numbers, whose keys are
+// >= 0x007fffff); key 0 is left for entries that take no part.  Then
+// "a ranks before b" is ka > kb || (ka == kb && ida < idb), which compiles
+// to compares and masks with no branches.
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   if (f != f) return 1u;

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void update_decide_kernel(
     int32_t *__restrict__ a_src, int32_t *__restrict__ a_count, int H, int W, int C, int T,
     int64_t n_sink, int shared, int32_t *status) {
   __shared__ int64_t xid[kMaxX];
-  __shared__ float xm[kMaxX];
+  __shared__ uint32_t xk[kMaxX];   // order key of the candidate's mass (order_key)
   __shared__ int32_t xsrc[kMaxX];   // >= 0: pool slot; < 0: window slot -1-w
   __shared__ int8_t xkeep[kMaxX];
   __shared__ int8_t cflag[kMaxLeave];
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void update_decide_kernel(
       m = 0.f;
       for (int h2 = 0; h2 < H; ++h2) m += mass_pool[(b0 + h2) * C + p];
     }
-    xm[p] = m;
+    xk[p] = order_key(m);
     xsrc[p] = p;
   }
   // stage the leaving slots' metadata (wl = -1 marks a slot out of range)
@@ -74,9 +74,9 @@ __global__ __launch_bounds__(256) void update_decide_kernel(
     const int64_t id = lid[c];
     bool ok = lwl[c] > 0;
 #pragma unroll 8
-    for (int p = 0; p < n_pool; ++p) ok = ok && xid[p] != id;
+    for (int p = 0; p < n_pool; ++p) ok &= xid[p] != id;
 #pragma unroll 8
-    for (int c2 = 0; c2 < c; ++c2) ok = ok && !(lwl[c2] > 0 && lid[c2] == id);
+    for (int c2 = 0; c2 < c; ++c2) ok &= !((lwl[c2] > 0) & (lid[c2] == id));
     cflag[c] = ok ? 1 : 0;
   }
   __syncthreads();
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void update_decide_kernel(
       m = 0.f;
       for (int h2 = 0; h2 < H; ++h2) m += mass_win[(b0 + h2) * W + w];
     }
-    xm[pos] = m;
+    xk[pos] = order_key(m);
     xsrc[pos] = -1 - w;
   }
   int nc = 0, np = 0;
@@ -115,16 +115,22 @@ __global__ __launch_bounds__(256) void update_decide_kernel(
       keep = true;
     } else if (n_pin > C) {  // more sinks than room: the C smallest ids
       int r = 0;
-      for (int y = 0; y < n_x; ++y) r += (xid[y] < n_sink) && (xid[y] < xid[x]);
+      for (int y = 0; y < n_x; ++y) r += (int)((xid[y] < n_sink) & (xid[y] < xid[x]));
       keep = pin && r < C;
     } else if (pin) {
       keep = true;
     } else {
       int r = 0;
-      const float mxx = xm[x];
+      const uint32_t kxx = xk[x];
       const int64_t ixx = xid[x];
+      // branch free: candidate y ranks before x iff its key is larger, or
+      // equal with a smaller id (mass descending, id ascending, NaN last)
 #pragma unroll 8
-      for (int y = 0; y < n_x; ++y) r += (xid[y] >= n_sink) && ranks_before(xm[y], xid[y], mxx, ixx);
+      for (int y = 0; y < n_x; ++y) {
+        const uint32_t ky = xk[y];
+        const int64_t iy = xid[y];
+        r += (int)((iy >= n_sink) & ((ky > kxx) | ((ky == kxx) & (iy < ixx))));
+      }
       keep = r < C - n_pin;
     }
     xkeep[x] = keep ? 1 : 0;
@@ -136,7 +142,7 @@ __global__ __launch_bounds__(256) void update_decide_kernel(
     if (!fr) continue;
     int pos = 0;
 #pragma unroll 8
-    for (int s2 = 0; s2 < s; ++s2) pos += (s2 >= n_pool || !xkeep[s2]);
+    for (int s2 = 0; s2 < s; ++s2) pos += (int)((s2 >= n_pool) | !xkeep[s2]);
     free_slot[pos] = s;
   }
   __syncthreads();
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(256) void update_decide_kernel(
     int pos = 0;  // rank among the admitted by id (ids are unique)
     const int64_t ixx = xid[x];
 #pragma unroll 8
-    for (int y = n_pool; y < n_x; ++y) pos += xkeep[y] && xid[y] < ixx;
+    for (int y = n_pool; y < n_x; ++y) pos += (int)((xkeep[y] != 0) & (xid[y] < ixx));
     const int slot = free_slot[pos];
     const int w = -1 - xsrc[x];
     a_slot[bh * C + pos] = slot;
