@@ -59,7 +59,7 @@ struct FwdArgs {
   // workgroups go to part_o / part_ml, and attn_fwd_merge_kernel combines
   // them after the forward launch.
   int split, NB, G;
-  int64_t U;
+  int P;  // pieces per query block in the split launch
   float *part_o, *part_ml;
 };
 
@@ -76,14 +76,13 @@ __device__ __forceinline__ void item_of_block(const FwdArgs &a, int &item) {
 // workgroups per CU.
 constexpr int kTile = 64;
 
-// Workgroup wg of a split launch covers block visits [u0, u1) of the
-// sequence item 0 entries 0..NB-1, item 1 entries 0..NB-1, ...; the
-// workgroup owning visit u is ((u + 1) G - 1) / U.
-__device__ __forceinline__ int64_t split_start(const FwdArgs &a, int wg) {
-  return (int64_t)wg * a.U / a.G;
-}
-__device__ __forceinline__ int split_owner(const FwdArgs &a, int64_t u) {
-  return (int)(((u + 1) * a.G - 1) / a.U);
+// Split launch: every query block's list cut into P equal ranges of
+// entries; workgroup wg takes range wg / n_items of query block
+// wg % n_items, so the pieces in flight together (consecutive workgroups,
+// one XCD) are the same range of consecutive query blocks of a head and
+// share its pool and current blocks in L2.  Piece wg writes partial slot wg.
+__device__ __forceinline__ int piece_start(const FwdArgs &a, int pc) {
+  return (int)((int64_t)pc * a.NB / a.P);
 }
 
 template <int D, int BT>
@@ -339,7 +338,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
     // piece of a split item: its partial goes to slot 2 wg (the workgroup's
     // first item) or 2 wg + 1 (its second), laid out [slot][dt][thread][16]
     // so that the merge of one dt reads a contiguous 16 KB
-    const int slot = 2 * wg + (split_start(a, wg) / a.NB == item ? 0 : 1);
+    const int slot = wg;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
       float *po = a.part_o + (((size_t)slot * (D / 32) + dt) * (2 * BT) + t) * 16;
@@ -382,13 +381,8 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kerne
     return;
   }
   if (wg >= a.G) return;
-  const int64_t u0 = split_start(a, wg), u1 = split_start(a, wg + 1);
-  for (int item = (int)(u0 / a.NB); (int64_t)item * a.NB < u1; ++item) {
-    const int64_t base = (int64_t)item * a.NB;
-    const int j0 = (int)(u0 > base ? u0 - base : 0);
-    const int j1 = (int)(u1 - base < a.NB ? u1 - base : a.NB);
-    fwd_segment<D, BT>(a, sh, K0, K1, V0, V1, wg, item, j0, j1);
-  }
+  const int pc = wg / a.n_items;
+  fwd_segment<D, BT>(a, sh, K0, K1, V0, V1, wg, wg % a.n_items, piece_start(a, pc), piece_start(a, pc + 1));
 }
 
 // Merge of the split pieces, one workgroup per (query block, 32 of the d
@@ -402,17 +396,13 @@ template <int D, int BT>
 __global__ __launch_bounds__(2 * BT) void attn_fwd_merge_kernel(FwdArgs a) {
   const int item = blockIdx.x / (D / 32), dt = blockIdx.x % (D / 32);
   if (item >= a.n_items) return;
-  const int64_t first_u = (int64_t)item * a.NB;
-  const int ga = split_owner(a, first_u), gb = split_owner(a, first_u + a.NB - 1);
-  if (ga == gb) return;
   const int i = item % a.QB;
   const size_t bh = item / a.QB;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int qrow = i * BT + wave * 32 + l32;
-  auto slot_of = [&](int gg) -> size_t {
-    return 2 * (size_t)gg + (split_start(a, gg) / a.NB == item ? 0 : 1);
-  };
+  auto slot_of = [&](int pc) -> size_t { return (size_t)pc * a.n_items + item; };
+  const int ga = 0, gb = a.P - 1;
   float M = -INFINITY;
   for (int gg = ga; gg <= gb; ++gg) M = fmaxf(M, a.part_ml[(slot_of(gg) * (2 * BT) + t) * 2]);
   float L = 0.f;
@@ -539,10 +529,11 @@ __global__ __launch_bounds__(kF32Tpr * BT) void attn_fwd_f32_kernel(FwdArgs a) {
 // Resident workgroups of the split launch: two per CU (LDS and VGPR
 // budget of the bf16 kernel), at most kSplitSlots.
 constexpr int kSplitSlots = 512;
-// Pieces per query block in the split launch.  More pieces keep more
-// loads in flight but each adds a partial to write and merge: forward on
-// 1-4 query blocks x 12 heads of the Wan cache took 47-55 us (cold
-// caches) with 8, 57-58 with 4, 50-70 with 16, 63-69 with 32.
+// Most pieces per query block in the split launch (fewer when fewer
+// resident slots per query block are free).  More pieces keep more loads
+// in flight but each adds a partial to write and merge: forward on 1-4
+// query blocks x 12 heads of the Wan cache took 41-51 us (cold caches)
+// with 8, against 57-58 with 4 and 50-70 with 16.
 constexpr int kMaxPieces = 8;
 
 static int split_slots() {
@@ -588,9 +579,9 @@ hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, co
   a.n_items = p.B * p.H * a.QB;
   a.NB = p.C + p.topk + a.QB;
   a.sl2 = scale * kLog2e;
-  a.U = (int64_t)a.n_items * a.NB;
   a.split = 0;
   a.G = 0;
+  a.P = 1;
   a.part_o = a.part_ml = nullptr;
   int n_wg = a.n_items;
   const int64_t slots = split_slots();
@@ -600,9 +591,11 @@ hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, co
   if (p.dtype == PBSA_BF16 && ws != nullptr && ws_bytes >= fwd_ws_bytes(p) &&
       2 * (int64_t)a.n_items <= slots) {
     a.split = 1;
-    const int64_t cap = (int64_t)a.n_items * kMaxPieces;
-    const int64_t g = a.U < slots ? a.U : slots;
-    a.G = (int)(g < cap ? g : cap);
+    int64_t pcs = slots / a.n_items;  // >= 2 here
+    if (pcs > kMaxPieces) pcs = kMaxPieces;
+    if (pcs > a.NB) pcs = a.NB;
+    a.P = (int)pcs;
+    a.G = a.n_items * a.P;
     char *w = reinterpret_cast<char *>(ws);
     a.part_o = reinterpret_cast<float *>(w);
     a.part_ml = reinterpret_cast<float *>(w + split_part_o_bytes(p));
