@@ -335,9 +335,9 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
   float l = (l4[0] + l4[1]) + (l4[2] + l4[3]);
   l += __shfl_xor(l, 32);
   if (j0 > 0 || j1 < a.NB) {
-    // piece of a split item: its partial goes to slot 2 wg (the workgroup's
-    // first item) or 2 wg + 1 (its second), laid out [slot][dt][thread][16]
-    // so that the merge of one dt reads a contiguous 16 KB
+    // piece of a split item: its partial goes to slot wg, laid out
+    // [slot][dt][thread][16] so that the merge of one dt reads a contiguous
+    // 16 KB
     const int slot = wg;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
@@ -390,8 +390,8 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kerne
 // the forward.  Two passes over the pieces in workgroup order: the max M of
 // their running maxima, then O = sum_g 2^(m_g - M) O_g / sum_g 2^(m_g - M) l_g.
 // The order is fixed, so the result does not depend on timing; the kernel
-// boundary orders the pieces' stores before these loads.  Query blocks that
-// one workgroup covered whole were written by the forward and are skipped.
+// boundary orders the pieces' stores before these loads.  A split launch
+// cuts every query block into P >= 2 non-empty pieces, so each has a partial.
 template <int D, int BT>
 __global__ __launch_bounds__(2 * BT) void attn_fwd_merge_kernel(FwdArgs a) {
   const int item = blockIdx.x / (D / 32), dt = blockIdx.x % (D / 32);
@@ -586,14 +586,14 @@ hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, co
   int n_wg = a.n_items;
   const int64_t slots = split_slots();
   // The split pays off only when one workgroup per query block would leave
-  // most resident slots idle: pieces that start mid-list lose the lockstep
-  // walk through the shared pool and current blocks that keeps them in L2.
-  if (p.dtype == PBSA_BF16 && ws != nullptr && ws_bytes >= fwd_ws_bytes(p) &&
-      2 * (int64_t)a.n_items <= slots) {
+  // most resident slots idle; otherwise the partials and their merge only
+  // add traffic.  It needs at least two pieces of at least one list entry
+  // each (a one-entry list is never split).
+  int64_t pcs = slots / a.n_items;
+  if (pcs > kMaxPieces) pcs = kMaxPieces;
+  if (pcs > a.NB) pcs = a.NB;
+  if (p.dtype == PBSA_BF16 && ws != nullptr && ws_bytes >= fwd_ws_bytes(p) && pcs >= 2) {
     a.split = 1;
-    int64_t pcs = slots / a.n_items;  // >= 2 here
-    if (pcs > kMaxPieces) pcs = kMaxPieces;
-    if (pcs > a.NB) pcs = a.NB;
     a.P = (int)pcs;
     a.G = a.n_items * a.P;
     char *w = reinterpret_cast<char *>(ws);

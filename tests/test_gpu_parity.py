@@ -113,6 +113,10 @@ CASES = {
     # W = 0, C = 0: the current chunk only
     "current_only": (syn.Shape(B=1, H=3, d=64, T=64, Nq=130, W=0, C=0, topk=0),
                      dict(sigma=1.0, win_len=[], pool_count=0)),
+    # a one-entry block list (no pool, no window, one ragged query block):
+    # the forward is never split, workspace or not
+    "one_entry_list": (syn.Shape(B=1, H=2, d=128, T=128, Nq=100, W=0, C=0, topk=0),
+                       dict(sigma=1.0, win_len=[], pool_count=0)),
     # a block list longer than the 128 entries staged in LDS (pool 12 + 140
     # selected + 3 current): the entries past it are resolved on the fly
     "long_list": (syn.Shape(B=1, H=2, d=128, T=64, Nq=3 * 64 - 5, W=150, C=12, topk=140),
@@ -191,13 +195,12 @@ def test_fine_mass_matches_oracle(name):
 
 
 @pytest.mark.parametrize("name", ["bf16_d128_T128_small", "bf16_d64_T64_multi", "bf16_d128_T64",
-                                  "empty_pool_and_window"])
+                                  "empty_pool_and_window", "one_entry_list"])
 def test_fwd_split_and_one_block_per_workgroup_agree(name):
-    """The forward with a split workspace (query blocks cut between
-    workgroups, merged by the last piece) and without one (one workgroup per
-    query block) both match the oracle; on these small problems the split
-    runs one list entry per workgroup, so every query block is merged from
-    one piece per entry."""
+    """The forward with a split workspace (every query block's list cut into
+    equal pieces, merged by a second kernel) and without one (one workgroup
+    per query block) both match the oracle; on these small problems the
+    split runs one list entry per piece.  A one-entry list is not split."""
     shape, kw = CASES[name]
     _log(f"case {name}")
     st = syn.make_state(shape, 23, pad_value=float("nan"), **kw)
