@@ -40,8 +40,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # FETCH 14,167 KiB, WRITE 28,304 KiB).  Valid only for the kernel source it
 # was measured on (sha1 over FWD_SOURCES below); reported as null once those
 # sources change.
-FWD_TRAFFIC = {"src_sha1": "f5eeac3249acd7144f58ef6a47bedb1149101520",
-               "fetch_kib": 59812.0, "write_kib": 14260.1,
+FWD_TRAFFIC = {"src_sha1": "b60acc3d03541d858374a9776148696afc243e4f",
+               "fetch_kib": 59786.3, "write_kib": 14260.0,
                "fetch_scale": 28302.0 / 14166.6, "write_scale": 28302.0 / 28304.3}
 
 

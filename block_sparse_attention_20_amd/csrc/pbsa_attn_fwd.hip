@@ -527,7 +527,8 @@ __global__ __launch_bounds__(kF32Tpr * BT) void attn_fwd_f32_kernel(FwdArgs a) {
 }
 
 // Resident workgroups of the split launch: two per CU (LDS and VGPR
-// budget of the bf16 kernel), at most kSplitSlots.
+// budget of the bf16 kernel), at most kSplitSlots.  A split launch runs at
+// most that many pieces, one workspace partial each.
 constexpr int kSplitSlots = 512;
 // Most pieces per query block in the split launch (fewer when fewer
 // resident slots per query block are free).  More pieces keep more loads
@@ -554,10 +555,10 @@ static int split_slots() {
 }
 
 static size_t split_part_o_bytes(const pbsa_problem &p) {
-  return align256((size_t)2 * kSplitSlots * (2 * p.T) * (p.d / 2) * sizeof(float));
+  return align256((size_t)kSplitSlots * (2 * p.T) * (p.d / 2) * sizeof(float));
 }
 static size_t split_part_ml_bytes(const pbsa_problem &p) {
-  return align256((size_t)2 * kSplitSlots * (2 * p.T) * 2 * sizeof(float));
+  return align256((size_t)kSplitSlots * (2 * p.T) * 2 * sizeof(float));
 }
 
 size_t fwd_ws_bytes(const pbsa_problem &p) {

@@ -167,12 +167,13 @@ int pbsa_block_mass(const pbsa_problem *p, float *mass_pool, float *mass_win, co
  * Workspace: optional.  With ws == NULL (or ws_bytes below
  * pbsa_workspace_size(p, PBSA_OP_FWD)) each query block runs in one
  * workgroup.  With a large enough 16-byte-aligned ws (bf16 only) and at
- * most half the GPU's resident workgroups' worth of query blocks, the
- * query-block x list-entry visits are split evenly over up to 8 workgroups
- * per query block; each piece leaves a partial in ws and a second kernel,
- * enqueued by the same call, merges them in a fixed order, so results stay
- * bitwise reproducible.  ws needs no initialisation; calls that share one
- * ws must not overlap in time (one stream is fine).
+ * most half the GPU's resident workgroups' worth of query blocks, every
+ * query block's list is cut into 2 to 8 equal ranges, one workgroup each;
+ * each piece leaves a partial in ws (fp32 O, running max and row sum of
+ * its 2T threads; at most 512 pieces) and a second kernel, enqueued by the
+ * same call, merges them in a fixed order, so results stay bitwise
+ * reproducible.  ws needs no initialisation; calls that share one ws must
+ * not overlap in time (one stream is fine).
  */
 int pbsa_attn_fwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const int32_t *sel,
                   const int32_t *sel_count, void *o, float *lse, void *ws, size_t ws_bytes,

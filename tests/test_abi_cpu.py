@@ -64,10 +64,10 @@ def test_validate_select_size_limit():
 
 def test_workspace_sizes():
     p = wan()
-    # forward: optional split workspace - partial O^T (fp32) and (max, sum)
-    # for two pieces per resident workgroup
+    # forward: optional split workspace - partial O^T (fp32, 64 per thread)
+    # and (max, sum) for each of at most 512 pieces of 256 threads
     ws_fwd = P.pbsa_workspace_size(p, P.PBSA_OP_FWD)
-    assert ws_fwd >= 2 * 512 * 256 * 64 * 4 + 2 * 512 * 256 * 2 * 4
+    assert ws_fwd >= 512 * 256 * 64 * 4 + 512 * 256 * 2 * 4
     f32 = wan(); f32.dtype = P.PBSA_F32
     assert P.pbsa_workspace_size(f32, P.PBSA_OP_FWD) == 0
     ws_sel = P.pbsa_workspace_size(p, P.PBSA_OP_SELECT)
