@@ -53,7 +53,7 @@ class PBSALayer:
         self.ws_select = P.workspace(self.prob, P.PBSA_OP_SELECT, device)
         self.ws_update = P.workspace(self.prob, P.PBSA_OP_UPDATE, device)
         self.ws_bwd = P.workspace(self.prob, P.PBSA_OP_BWD, device)
-        # forward workspace: "own" allocates one (balanced split launch), None
+        # forward workspace: "own" allocates one (split launch for few query blocks), None
         # runs one workgroup per query block, a tensor is shared (layers that
         # run one after another on one stream can share it)
         self.ws_fwd = P.workspace(self.prob, P.PBSA_OP_FWD, device) if isinstance(ws_fwd, str) else ws_fwd

@@ -254,8 +254,8 @@ def test_short_chunk_split_matches_oracle(qb):
 
 def test_fwd_split_workspace_needs_no_initialisation():
     """The split forward's workspace may hold anything (here: bytes of an
-    earlier use, then random bytes): arrival counters only count words
-    tagged with the running launch, so the result matches a clean run."""
+    earlier use, then random bytes): every piece writes its partial before
+    the merge kernel reads it, so the result matches a clean run."""
     shape, kw = CASES["bf16_d64_T64_multi"]
     st = syn.make_state(shape, 31, **kw)
     L = run(shape, st)
