@@ -14,8 +14,8 @@ needed by the next chunk.  Inputs are synthetic
 
 Prints ONE JSON line: attention TFLOP/s over the whole step (algorithmic
 forward FLOPs 4*d*sum_rows|U_r| / step time), per-chunk latency, the forward
-kernel's roofline position (HIP events around every forward launch inside
-the timed region), a training step (batch 2, fwd + bwd) and the fp64 CPU
+kernel's roofline position (HIP events around a rotating sample of the
+forward launches inside the timed region, every layer sampled), a training step (batch 2, fwd + bwd) and the fp64 CPU
 oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -581,8 +581,8 @@ def main():
                     help="only the coarse vs exact block-mass comparison (its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: PBSA shards by head with no exchange, and this build "
-              "runs on a single MI355X (use --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU only (use --gpus 1): PBSA would shard by head with no "
+              "exchange between GPUs, so the single-GPU rate is the per-GPU figure.", file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
