@@ -195,7 +195,7 @@ def test_fine_mass_matches_oracle(name):
 
 
 @pytest.mark.parametrize("name", ["bf16_d128_T128_small", "bf16_d64_T64_multi", "bf16_d128_T64",
-                                  "empty_pool_and_window", "one_entry_list"])
+                                  "bf16_d64_T128", "empty_pool_and_window", "one_entry_list"])
 def test_fwd_split_and_one_block_per_workgroup_agree(name):
     """The forward with a split workspace (every query block's list cut into
     equal pieces, merged by a second kernel) and without one (one workgroup
