@@ -523,9 +523,14 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dkv_kernel(BwdA
     const size_t off = (bh * a.W + w) * (size_t)(BT * D);
     kp = a.k_win + off; vp = a.v_win + off; dkp = a.dk_win + off; dvp = a.dv_win + off;
     len = max(0, min(a.win_len[w], BT));
-    list_base = a.qptr[bh * (a.W + 1) + w];
-    nq = a.qptr[bh * (a.W + 1) + w + 1] - list_base;
     all_q = false;
+    // with topk == 0 no query block selects any window slot, and the
+    // inverse lists are not built (the launcher skips them): read nothing
+    nq = 0;
+    if (a.topk > 0) {
+      list_base = a.qptr[bh * (a.W + 1) + w];
+      nq = a.qptr[bh * (a.W + 1) + w + 1] - list_base;
+    }
   }
   if (all_q) nq = a.QB;
   if (len == 0) nq = 0;

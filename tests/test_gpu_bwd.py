@@ -74,6 +74,15 @@ CASES = {
     "long_list": (syn.Shape(B=1, H=1, d=64, T=64, Nq=3 * 64 - 5, W=150, C=10, topk=140),
                   dict(sigma=1.0, shift=1.0, n_planted=4, win_len=[64] * 70 + [0, 23] + [64] * 78,
                        pool_count=10)),
+    # a block list longer than the 128 entries staged in LDS at d128, blocks
+    # of 128 (pool 6 + 124 selected + 2 current)
+    "long_list_d128_T128": (syn.Shape(B=1, H=1, d=128, T=128, Nq=2 * 128 - 30, W=130, C=6, topk=124),
+                            dict(sigma=1.0, shift=1.0, n_planted=4,
+                                 win_len=[128] * 60 + [0, 72] + [128] * 67 + [5], pool_count=6)),
+    # a window but no selection (k = 0): no inverse lists are built, and every
+    # window gradient must come out exactly zero
+    "window_topk0": (syn.Shape(B=1, H=2, d=64, T=64, Nq=2 * 64 - 3, W=4, C=2, topk=0),
+                     dict(sigma=1.0, win_len=[64, 64, 17, 64], pool_count=[2, 1])),
 }
 
 
@@ -90,7 +99,8 @@ def test_bwd_matches_oracle(name):
     # the oracle leaves NaN padding of the inputs alone; its gradients there are 0
     compare(g, ref, name)
     # unselected window slots, invalid pool slots and padding rows are exact zeros
-    chosen = {(b, h): set(sel[b, h][sel[b, h] >= 0].tolist()) for b, h in np.ndindex(shape.B, shape.H)}
+    chosen = {(b, h): {int(w) for i in range(shape.QB) for w in sel[b, h, i, :cnt[b, h, i]]}
+              for b, h in np.ndindex(shape.B, shape.H)}
     wl = st["win_len"].tolist()
     for b, h in np.ndindex(shape.B, shape.H):
         for w in range(shape.W):
