@@ -34,6 +34,11 @@ MUTATIONS = [
      ["test_fwd_dense_limit_equals_textbook_attention"]),
     ("block_mean", "return rows.sum(axis=0) / n", "return rows.sum(axis=0) / max(n, 4)",
      ["test_block_mean_closed_form", "test_pooled_queries_ragged_tail"]),
+    ("pooled_slots", "out[idx] = block_mean(k_slots[idx][:n])",
+     "out[idx] = k_slots[idx][:n].sum(axis=0) / k_slots.shape[-2]",
+     ["test_pooled_slots_ragged_closed_form"]),
+    ("pooled_slots", "out[idx] = block_mean(k_slots[idx][:n])", "out[idx] = block_mean(k_slots[idx])",
+     ["test_pooled_slots_ragged_closed_form"]),
     ("coarse_logit", "return float(scale * np.dot(_f64(qbar), _f64(kbar)))",
      "return float(np.dot(_f64(qbar), _f64(kbar)))",
      ["test_topk_scale_sign_matters", "test_coarse_scores_with_T1_are_token_logits"]),

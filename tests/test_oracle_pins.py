@@ -48,6 +48,39 @@ def test_pooled_queries_ragged_tail():
     assert qb[0, 0, 2, 0] == 8.0
 
 
+def test_pooled_slots_ragged_closed_form():
+    # slot rows r*a + c for r < len (mean a (len-1)/2 + c, exactly); the
+    # padding rows after len hold a large finite value, so a mean that reads
+    # them, or divides a short slot's sum by T, is off by far more than the
+    # tolerance.  An empty slot has no representative (NaN).
+    T, d = 8, 3
+    a = np.array([1.0, -2.0, 0.5]); c = np.array([3.0, 0.0, -1.0])
+    lens = np.array([8, 3, 1, 0, 5])
+    k = np.full((1, 1, len(lens), T, d), 1000.0)
+    for w, n in enumerate(lens):
+        k[0, 0, w, :n] = np.arange(n)[:, None] * a + c
+    got = po.pooled_slots(k, lens[None, None, :])
+    for w, n in enumerate(lens):
+        if n == 0:
+            assert np.isnan(got[0, 0, w]).all()
+        else:
+            np.testing.assert_allclose(got[0, 0, w], a * (n - 1) / 2 + c, rtol=0, atol=1e-12)
+    # the same means seen through the coarse logits of select(): all queries
+    # are e0, so slot w's logit is scale * (its mean's first coordinate)
+    W = len(lens)
+    shape, st = small_state(B=1, H=1, d=d, T=T, Nq=2 * T, W=W, C=2, topk=2,
+                            win_len=lens.tolist(), pool_count=0, pad_value=0.0)
+    st["q"][:] = 0; st["q"][..., 0] = 1.0
+    st["k_win"][:] = torch.from_numpy(k.astype(np.float32))
+    r = po.select(st, 2, 0.5, T)
+    for w, n in enumerate(lens):
+        if n > 0:
+            np.testing.assert_allclose(r["s_win"][0, 0, :, w], 0.5 * (a[0] * (n - 1) / 2 + c[0]),
+                                       rtol=0, atol=1e-12)
+        else:
+            assert np.isnan(r["s_win"][0, 0, :, w]).all()
+
+
 def test_coarse_scores_with_T1_are_token_logits():
     # T = 1: every block is one token, so coarse logits are the token logits
     shape, st = small_state(T=1, Nq=5, W=6, C=2, topk=6, d=8, H=1)
