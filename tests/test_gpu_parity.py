@@ -123,6 +123,11 @@ CASES = {
                   dict(sigma=1.0, shift=1.0, n_planted=4,
                        win_len=[64] * 40 + [0, 30] + [64] * 100 + [17] + [64] * 7,
                        pool_count=[12, 7])),
+    # the same at the benchmark's tile shape (d128, blocks of 128): pool 8 +
+    # 130 selected + 2 current = 140 entries, past the 128 staged in LDS
+    "long_list_d128_T128": (syn.Shape(B=1, H=1, d=128, T=128, Nq=2 * 128 - 30, W=140, C=8, topk=130),
+                            dict(sigma=1.0, shift=1.0, n_planted=4,
+                                 win_len=[128] * 60 + [0, 72] + [128] * 77 + [5], pool_count=8)),
 }
 
 
@@ -161,7 +166,8 @@ def test_select_and_fwd_match_oracle(name):
 
 @pytest.mark.parametrize("name", ["bf16_d128_T128_small", "bf16_d64_T64_multi", "bf16_d64_T128",
                                   "bf16_d128_T64", "f32_d64_T64", "f32_d128_T128",
-                                  "empty_pool_and_window", "topk_covers_window", "long_list"])
+                                  "empty_pool_and_window", "topk_covers_window", "long_list",
+                                  "long_list_d128_T128"])
 def test_fine_mass_matches_oracle(name):
     """Exact block masses from the forward's lse against the fp64 oracle on
     the GPU's own selection.  Bar: 5e-3 of the largest mass (bf16 rounding is
@@ -474,8 +480,8 @@ def test_bad_device_metadata_is_clamped_and_flagged():
 def test_wan_chunk_full_size(unscaled):
     """The Wan2.1-1.3B-shaped chunk (12 heads, 4680 tokens, window 74, pool 32,
     top-16) at full size, in the launch configuration the benchmark times:
-    full selection and masses against the oracle; attention on sampled query
-    blocks (first, middle, the ragged tail) of several heads."""
+    full selection and masses against the oracle, and O / LSE of every row
+    of every head (all 444 query blocks)."""
     _log(f"wan chunk unscaled={unscaled}")
     shape = syn.WAN_CHUNK
     st = syn.wan_chunk_state(0, unscaled=unscaled)
@@ -490,17 +496,63 @@ def test_wan_chunk_full_size(unscaled):
         assert set(st["planted"]) <= set(gsel[idx].tolist())
     np.testing.assert_allclose(L.t["mass_pool"].cpu().numpy(), r["mass_pool"], rtol=1e-4, atol=1e-6)
     np.testing.assert_allclose(L.t["mass_win"].cpu().numpy(), r["mass_win"], rtol=1e-4, atol=1e-6)
-    blocks = [(0, h, i) for h in (0, 5, 11) for i in (0, 17, 36)]
-    f = po.attn_fwd(st, gsel, gcnt, scale, shape.T, blocks=blocks)
+    f = po.attn_fwd(st, gsel, gcnt, scale, shape.T)
     o = L.t["o"].float().cpu().numpy()
-    rows = np.concatenate([np.arange(i * 128, min(4680, i * 128 + 128)) for _, _, i in blocks[:3]])
-    got = np.concatenate([o[0, h, rows] for h in (0, 5, 11)])
-    ref = np.concatenate([f["o"][0, h, rows] for h in (0, 5, 11)])
-    check_close_bf16(got, ref, f"wan chunk (unscaled={unscaled})")
+    assert not np.isnan(f["o"]).any()
+    check_close_bf16(o, f["o"], f"wan chunk, all rows (unscaled={unscaled})")
     lse = L.t["lse"].cpu().numpy()
-    lref = np.concatenate([f["lse"][0, h, rows] for h in (0, 5, 11)])
-    lgot = np.concatenate([lse[0, h, rows] for h in (0, 5, 11)])
-    assert np.abs(lgot - lref).max() <= 2e-3
+    assert np.abs(lse - f["lse"]).max() <= 2e-3
+    assert L.status_bits() == 0
+
+
+def test_tiny_f32_config_matches_oracle():
+    """The tiny fp32 configuration itself (1 head of 64, blocks of 64, a
+    256-token chunk, window 32, pool 4, top-4, seed 0, two planted window
+    blocks): selection, pooled keys and masses, the forward (<= 1e-4) on the
+    fp32 path, and the Top-C update with window slots 0-3 leaving, all
+    against the oracle."""
+    shape = syn.TINY_F32
+    st = syn.tiny_f32_state()
+    L = run(shape, st)
+    scale = eff_scale(shape, 0.0)
+    r = po.select(st, shape.topk, scale, shape.T)
+    gsel = L.t["sel"].cpu().numpy(); gcnt = L.t["sel_count"].cpu().numpy()
+    n_tie = check_selection(L, r, st, shape.topk)
+    assert n_tie == 0
+    for idx in np.ndindex(*gcnt.shape):
+        assert set(st["planted"]) <= set(gsel[idx].tolist())
+    np.testing.assert_allclose(L.t["kbar_cur"].cpu().numpy(), r["kbar_cur"], rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(L.t["kbar_win"].cpu().numpy(), r["kbar_win"], rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(L.t["mass_pool"].cpu().numpy(), r["mass_pool"], rtol=1e-4, atol=1e-6)
+    np.testing.assert_allclose(L.t["mass_win"].cpu().numpy(), r["mass_win"], rtol=1e-4, atol=1e-6)
+    f = po.attn_fwd(st, gsel, gcnt, scale, shape.T)
+    o = L.t["o"].cpu().numpy()
+    err = np.abs(o - f["o"]).max()
+    _log(f"tiny fp32 forward: max-abs {err:.3e}")
+    assert err <= 1e-4
+    assert np.abs(L.t["lse"].cpu().numpy() - f["lse"]).max() <= 1e-5
+    # the update: the oldest four window slots leave, the pool (4, full) keeps
+    # the four best of 8 candidates
+    mp = L.t["mass_pool"].cpu().numpy(); mw = L.t["mass_win"].cpu().numpy()
+    kbw = L.t["kbar_win"].cpu().numpy(); kbp = L.t["kbar_pool"].cpu().numpy()
+    before_k = L.t["k_pool"].clone()
+    leaving = [0, 1, 2, 3]
+    L.update(torch.tensor(leaving, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    u = po.memory_update(st, mp, mw, leaving, 0, kbar_win=kbw, kbar_pool=kbp)
+    np.testing.assert_array_equal(L.t["pool_count"].cpu().numpy(), u["pool_count"])
+    n = int(u["pool_count"][0, 0])
+    np.testing.assert_array_equal(L.t["pool_id"][0, 0, :n].cpu().numpy(), u["pool_id"][0, 0, :n])
+    np.testing.assert_array_equal(L.t["pool_len"][0, 0, :n].cpu().numpy(), u["pool_len"][0, 0, :n])
+    np.testing.assert_array_equal(L.t["kbar_pool"][0, 0, :n].cpu().numpy(), u["kbar_pool"][0, 0, :n])
+    admitted = {s_ for s_, _ in u["admitted"][(0, 0)]}
+    for slot, w in u["admitted"][(0, 0)]:
+        assert torch.equal(L.t["k_pool"][0, 0, slot], L.t["k_win"][0, 0, w])
+        assert torch.equal(L.t["v_pool"][0, 0, slot], L.t["v_win"][0, 0, w])
+    for slot in range(shape.C):
+        if slot not in admitted:
+            assert torch.equal(L.t["k_pool"][0, 0, slot], before_k[0, 0, slot])
+    assert L.status_bits() == 0
 
 
 def _one_head(st, h):
