@@ -36,7 +36,8 @@
 //     blocks, the list visits are split evenly over up to 8 workgroups per
 //     query block; each piece writes a partial and attn_fwd_merge_kernel
 //     combines them after the launch, in a fixed order.
-// fp32 path: vector FMA version of the same walk (small problems).
+// fp32 path: the same walk on fp32 MFMA (v_mfma_f32_32x32x2_f32), with the
+// same split and merge (small problems).
 #include "pbsa_common.h"
 #include "pbsa_internal.h"
 #include "pbsa_tiles.h"
@@ -392,7 +393,7 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kerne
 // The order is fixed, so the result does not depend on timing; the kernel
 // boundary orders the pieces' stores before these loads.  A split launch
 // cuts every query block into P >= 2 non-empty pieces, so each has a partial.
-template <int D, int BT>
+template <int D, int BT, typename TOut>
 __global__ __launch_bounds__(2 * BT) void attn_fwd_merge_kernel(FwdArgs a) {
   const int item = blockIdx.x / (D / 32), dt = blockIdx.x % (D / 32);
   if (item >= a.n_items) return;
@@ -425,105 +426,182 @@ __global__ __launch_bounds__(2 * BT) void attn_fwd_merge_kernel(FwdArgs a) {
   }
   if (qrow >= a.Nq) return;
   const float inv = 1.f / L;
-  uint16_t *op = (uint16_t *)a.o + (bh * a.Nq + qrow) * (size_t)D;
+  if constexpr (std::is_same<TOut, float>::value) {
+    float *op = (float *)a.o + (bh * a.Nq + qrow) * (size_t)D;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    u32x2 pk;
-    pk[0] = pack_bf16x2(acc[4 * jj] * inv, acc[4 * jj + 1] * inv);
-    pk[1] = pack_bf16x2(acc[4 * jj + 2] * inv, acc[4 * jj + 3] * inv);
-    *reinterpret_cast<u32x2 *>(op + dt * 32 + 8 * jj + 4 * g) = pk;
+    for (int jj = 0; jj < 4; ++jj)
+      *reinterpret_cast<f32x4 *>(op + dt * 32 + 8 * jj + 4 * g) =
+          f32x4{acc[4 * jj] * inv, acc[4 * jj + 1] * inv, acc[4 * jj + 2] * inv, acc[4 * jj + 3] * inv};
+  } else {
+    uint16_t *op = (uint16_t *)a.o + (bh * a.Nq + qrow) * (size_t)D;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      u32x2 pk;
+      pk[0] = pack_bf16x2(acc[4 * jj] * inv, acc[4 * jj + 1] * inv);
+      pk[1] = pack_bf16x2(acc[4 * jj + 2] * inv, acc[4 * jj + 3] * inv);
+      *reinterpret_cast<u32x2 *>(op + dt * 32 + 8 * jj + 4 * g) = pk;
+    }
   }
   if (dt == 0 && g == 0 && a.lse) a.lse[bh * a.Nq + qrow] = (M + log2f(L)) * kLn2;
 }
 
-// fp32 vector path: kF32Tpr threads per query row, each owning D / kF32Tpr
-// of the dims (a dot product is a partial sum per thread, reduced over the
-// row's lanes with xor shuffles).  One workgroup per query block; K and V
-// of one list block staged in LDS at a time; online softmax per 16 keys.
-// On the tiny configuration (1 head x 64, 4 query blocks of 64) 8 threads
-// per row took 171 us, 16 threads 205 us, 2 threads 415 us.
-constexpr int kF32Tpr = 8;
-
+// fp32 path (v_mfma_f32_32x32x2_f32), for the small fp32 problems.  Same
+// work split as the bf16 kernel (a whole query block, or a piece of its list
+// in the split launch, per workgroup; wave w owns query rows [32w, 32w+32))
+// and the same accumulator layout, so the pieces go through the same merge.
+//   - the contraction order over d is free, so k-step s of S^T = K Q^T takes
+//     dims s (lanes 0-31) and D/2 + s (lanes 32-63): a lane's Q values and
+//     its K reads are then contiguous runs (16-byte LDS reads, four k-steps
+//     each), and Q stays in D/2 registers per lane;
+//   - likewise k-step s of O^T = V^T P^T takes, in lane half g, the token
+//     held in S^T accumulator element s of that half, so P needs no exchange
+//     between lanes: the exponential of element s is the B operand as is;
+//   - K and V go through LDS in 64-token tiles with padded rows (K: D + 4,
+//     V: D + 8 floats), which makes both read patterns bank-conflict free.
 template <int D, int BT>
-__global__ __launch_bounds__(kF32Tpr * BT) void attn_fwd_f32_kernel(FwdArgs a) {
-  constexpr int NT = kF32Tpr * BT;
-  constexpr int DH = D / kF32Tpr;
-  __shared__ __attribute__((aligned(16))) float Ks[BT * D];
-  __shared__ __attribute__((aligned(16))) float Vs[BT * D];
-  int item;
-  item_of_block(a, item);
-  if (item >= a.n_items) return;
+__device__ __forceinline__ void fwd_f32_segment(const FwdArgs &a, float *Ks, float *Vs, int wg,
+                                                int item, int j0, int j1) {
+  constexpr int NT = 2 * BT, TT = 64;
+  constexpr int SK = D + 4, SV = D + 8;
   const int i = item % a.QB;
   const size_t bh = item / a.QB;
-  const int t = threadIdx.x, r = t / kF32Tpr, part = t % kF32Tpr;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
   int n_pool, sc;
   const int nb = clamp_counts(a, bh, i, n_pool, sc);
-  const int qrow = i * BT + r;
-  float qv[DH], ov[DH];
-  const float *qp = (const float *)a.q + (bh * a.Nq + qrow) * (size_t)D + part * DH;
+  const int jend = min(j1, nb);
+  const int qrow = i * BT + wave * 32 + l32;
+  // this lane's query row: dims [g D/2, g D/2 + D/2), the B operand of S^T
+  float qv[D / 2];
+  {
+    const float *qp = (const float *)a.q + (bh * a.Nq + (qrow < a.Nq ? qrow : 0)) * (size_t)D + g * (D / 2);
 #pragma unroll
-  for (int x = 0; x < DH; ++x) {
-    qv[x] = qrow < a.Nq ? qp[x] : 0.f;
-    ov[x] = 0.f;
+    for (int s4 = 0; s4 < D / 8; ++s4) {
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (qrow < a.Nq) v = *reinterpret_cast<const f32x4 *>(qp + 4 * s4);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qv[4 * s4 + c] = v[c];
+    }
   }
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
   float m = -INFINITY, l = 0.f;
   const float sl2 = a.sl2;
-  for (int j = 0; j < nb; ++j) {
+  for (int j = j0; j < jend; ++j) {
     const float *kp, *vp;
     int len;
     resolve_block<float, D, BT>(a, bh, i, n_pool, sc, j, kp, vp, len);
-    __syncthreads();
-    for (int e = t * 4; e < BT * D; e += NT * 4) {
-      const int row = e / D;
-      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-      if (row < len) {
-        kv = *reinterpret_cast<const f32x4 *>(kp + e);
-        vv = *reinterpret_cast<const f32x4 *>(vp + e);
+    for (int h0 = 0; h0 < len; h0 += TT) {
+      const int tlen = min(TT, len - h0);
+      __syncthreads();  // every wave is done with the previous tile
+      for (int e = t; e < TT * D / 4; e += NT) {
+        const int row = e / (D / 4), c4 = e % (D / 4);
+        f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+        if (row < tlen) {  // rows past the block's length are zeros, never its padding
+          kv = *reinterpret_cast<const f32x4 *>(kp + (size_t)(h0 + row) * D + 4 * c4);
+          vv = *reinterpret_cast<const f32x4 *>(vp + (size_t)(h0 + row) * D + 4 * c4);
+        }
+        *reinterpret_cast<f32x4 *>(&Ks[row * SK + 4 * c4]) = kv;
+        *reinterpret_cast<f32x4 *>(&Vs[row * SV + 4 * c4]) = vv;
       }
-      *reinterpret_cast<f32x4 *>(&Ks[e]) = kv;
-      *reinterpret_cast<f32x4 *>(&Vs[e]) = vv;
-    }
-    __syncthreads();
-    for (int u0 = 0; u0 < len; u0 += 16) {
-      float s[16];
+      __syncthreads();
+      // S^T[token][query] over the tile's two 32-token halves
+      f32x16 sacc[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[tt][e] = 0.f;
+        const float *kr = &Ks[(tt * 32 + l32) * SK + g * (D / 2)];
+#pragma unroll
+        for (int s4 = 0; s4 < D / 8; ++s4) {
+          const f32x4 kf = *reinterpret_cast<const f32x4 *>(kr + 4 * s4);
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[c], qv[4 * s4 + c], sacc[tt], 0, 0, 0);
+        }
+      }
+      // element e of half tt is token tt*32 + 8 (e / 4) + 4 g + e % 4
       float mx = -INFINITY;
 #pragma unroll
-      for (int uu = 0; uu < 16; ++uu) {
-        const int u = u0 + uu;
-        const float *kr = &Ks[(u < BT ? u : 0) * D + part * DH];
-        float acc = 0.f;
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int x = 0; x < DH; ++x) acc += qv[x] * kr[x];
-#pragma unroll
-        for (int o = 1; o < kF32Tpr; o <<= 1) acc += __shfl_xor(acc, o);
-        s[uu] = u < len ? acc * sl2 : -INFINITY;
-        mx = fmaxf(mx, s[uu]);
-      }
+        for (int e = 0; e < 16; ++e) {
+          const int tok = tt * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+          if (tok >= tlen) sacc[tt][e] = -INFINITY;
+          mx = fmaxf(mx, sacc[tt][e]);
+        }
+      mx = half_swap_max(mx) * sl2;
       const float mnew = fmaxf(m, mx);
       const float muse = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2f(m - muse);
+      const float alpha = __builtin_amdgcn_exp2f(m - muse);  // m = -inf -> 0
       m = mnew;
       l *= alpha;
 #pragma unroll
-      for (int x = 0; x < DH; ++x) ov[x] *= alpha;
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int uu = 0; uu < 16; ++uu) {
-        const int u = u0 + uu;
-        const float p = exp2f(s[uu] - muse);
-        l += p;
-        const float *vr = &Vs[(u < BT ? u : 0) * D + part * DH];
+        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+      // O^T += V^T P^T: k-step s of half tt pairs the tokens of element s
 #pragma unroll
-        for (int x = 0; x < DH; ++x) ov[x] += p * vr[x];
-      }
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          const float p = __builtin_amdgcn_exp2f(sacc[tt][s] * sl2 - muse);
+          l += p;
+          const int tok = tt * 32 + 8 * (s >> 2) + 4 * g + (s & 3);
+          const float *vr = &Vs[tok * SV + l32];
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[dt * 32], p, oacc[dt], 0, 0, 0);
+        }
     }
   }
+  l += __shfl_xor(l, 32);
+  if (j0 > 0 || j1 < a.NB) {
+    // piece of a split item: partial slot wg, the bf16 kernel's layout
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      float *po = a.part_o + (((size_t)wg * (D / 32) + dt) * (2 * BT) + t) * 16;
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        *reinterpret_cast<f32x4 *>(po + 4 * e4) =
+            f32x4{oacc[dt][4 * e4], oacc[dt][4 * e4 + 1], oacc[dt][4 * e4 + 2], oacc[dt][4 * e4 + 3]};
+    }
+    float *pm = a.part_ml + ((size_t)wg * (2 * BT) + t) * 2;
+    pm[0] = m;
+    pm[1] = l;
+    return;
+  }
   if (qrow < a.Nq) {
-    float *op = (float *)a.o + (bh * a.Nq + qrow) * (size_t)D + part * DH;
+    float *op = (float *)a.o + (bh * a.Nq + qrow) * (size_t)D;
     const float inv = 1.f / l;
 #pragma unroll
-    for (int x = 0; x < DH; ++x) op[x] = ov[x] * inv;
-    if (part == 0 && a.lse) a.lse[bh * a.Nq + qrow] = (m + log2f(l)) * kLn2;
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<f32x4 *>(op + dt * 32 + 8 * jj + 4 * g) =
+            f32x4{oacc[dt][4 * jj] * inv, oacc[dt][4 * jj + 1] * inv, oacc[dt][4 * jj + 2] * inv,
+                  oacc[dt][4 * jj + 3] * inv};
+    if (g == 0 && a.lse) a.lse[bh * a.Nq + qrow] = (m + log2f(l)) * kLn2;
   }
+}
+
+template <int D, int BT>
+__global__ __launch_bounds__(2 * BT) void attn_fwd_f32_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float Ks[64 * (D + 4)];
+  __shared__ __attribute__((aligned(16))) float Vs[64 * (D + 8)];
+  int wg;
+  item_of_block(a, wg);
+  if (!a.split) {
+    if (wg < a.n_items) fwd_f32_segment<D, BT>(a, Ks, Vs, wg, wg, 0, a.NB);
+    return;
+  }
+  if (wg >= a.G) return;
+  const int pc = wg / a.n_items;
+  fwd_f32_segment<D, BT>(a, Ks, Vs, wg, wg % a.n_items, piece_start(a, pc), piece_start(a, pc + 1));
 }
 
 // Resident workgroups of the split launch: two per CU (LDS and VGPR
@@ -536,6 +614,9 @@ constexpr int kSplitSlots = 512;
 // query blocks x 12 heads of the Wan cache took 41-51 us (cold caches)
 // with 8, against 57-58 with 4 and 50-70 with 16.
 constexpr int kMaxPieces = 8;
+// The fp32 path serves small problems, where a query block's list is a few
+// blocks: one piece per list entry, up to this many.
+constexpr int kMaxPiecesF32 = 16;
 
 static int split_slots() {
   // per device, filled on first use; concurrent first calls store the same
@@ -562,7 +643,6 @@ static size_t split_part_ml_bytes(const pbsa_problem &p) {
 }
 
 size_t fwd_ws_bytes(const pbsa_problem &p) {
-  if (p.dtype != PBSA_BF16) return 0;
   return split_part_o_bytes(p) + split_part_ml_bytes(p);
 }
 
@@ -591,9 +671,10 @@ hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, co
   // add traffic.  It needs at least two pieces of at least one list entry
   // each (a one-entry list is never split).
   int64_t pcs = slots / a.n_items;
-  if (pcs > kMaxPieces) pcs = kMaxPieces;
+  const int max_pieces = p.dtype == PBSA_BF16 ? kMaxPieces : kMaxPiecesF32;
+  if (pcs > max_pieces) pcs = max_pieces;
   if (pcs > a.NB) pcs = a.NB;
-  if (p.dtype == PBSA_BF16 && ws != nullptr && ws_bytes >= fwd_ws_bytes(p) && pcs >= 2) {
+  if (ws != nullptr && ws_bytes >= fwd_ws_bytes(p) && pcs >= 2) {
     a.split = 1;
     a.P = (int)pcs;
     a.G = a.n_items * a.P;
@@ -605,29 +686,22 @@ hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, co
   a.per_xcd = (n_wg + 7) / 8;
   const dim3 grid(8 * a.per_xcd);
   const dim3 block(2 * p.T);
-#define PBSA_FWD_CASE(DT, D_, T_, KERN)                                              \
-  if (p.dtype == DT && p.d == D_ && p.T == T_) {                                     \
-    KERN<D_, T_><<<grid, block, 0, st>>>(a);                                         \
-    if (a.split)                                                                     \
-      attn_fwd_merge_kernel<D_, T_><<<dim3(a.n_items * (D_ / 32)), block, 0, st>>>(a); \
-    return hipGetLastError();                                                        \
+#define PBSA_FWD_CASE(DT, TOUT, D_, T_, KERN)                                              \
+  if (p.dtype == DT && p.d == D_ && p.T == T_) {                                           \
+    KERN<D_, T_><<<grid, block, 0, st>>>(a);                                               \
+    if (a.split)                                                                           \
+      attn_fwd_merge_kernel<D_, T_, TOUT><<<dim3(a.n_items * (D_ / 32)), block, 0, st>>>(a); \
+    return hipGetLastError();                                                              \
   }
-  PBSA_FWD_CASE(PBSA_BF16, 128, 128, attn_fwd_bf16_kernel)
-  PBSA_FWD_CASE(PBSA_BF16, 64, 128, attn_fwd_bf16_kernel)
-  PBSA_FWD_CASE(PBSA_BF16, 128, 64, attn_fwd_bf16_kernel)
-  PBSA_FWD_CASE(PBSA_BF16, 64, 64, attn_fwd_bf16_kernel)
+  PBSA_FWD_CASE(PBSA_BF16, uint16_t, 128, 128, attn_fwd_bf16_kernel)
+  PBSA_FWD_CASE(PBSA_BF16, uint16_t, 64, 128, attn_fwd_bf16_kernel)
+  PBSA_FWD_CASE(PBSA_BF16, uint16_t, 128, 64, attn_fwd_bf16_kernel)
+  PBSA_FWD_CASE(PBSA_BF16, uint16_t, 64, 64, attn_fwd_bf16_kernel)
+  PBSA_FWD_CASE(PBSA_F32, float, 128, 128, attn_fwd_f32_kernel)
+  PBSA_FWD_CASE(PBSA_F32, float, 64, 128, attn_fwd_f32_kernel)
+  PBSA_FWD_CASE(PBSA_F32, float, 128, 64, attn_fwd_f32_kernel)
+  PBSA_FWD_CASE(PBSA_F32, float, 64, 64, attn_fwd_f32_kernel)
 #undef PBSA_FWD_CASE
-  const dim3 block_f32(kF32Tpr * p.T);
-#define PBSA_FWD_F32_CASE(D_, T_)                                            \
-  if (p.dtype == PBSA_F32 && p.d == D_ && p.T == T_) {                       \
-    attn_fwd_f32_kernel<D_, T_><<<grid, block_f32, 0, st>>>(a);              \
-    return hipGetLastError();                                                \
-  }
-  PBSA_FWD_F32_CASE(128, 128)
-  PBSA_FWD_F32_CASE(64, 128)
-  PBSA_FWD_F32_CASE(128, 64)
-  PBSA_FWD_F32_CASE(64, 64)
-#undef PBSA_FWD_F32_CASE
   return hipErrorInvalidValue;
 }
 

@@ -46,7 +46,7 @@
  *
  * Supported: dtype PBSA_BF16 with d in {64, 128} and T in {64, 128}
  * (bf16 MFMA, fp32 accumulate and softmax); dtype PBSA_F32 with d in
- * {64, 128}, T in {64, 128} (fp32 vector path) for every call except
+ * {64, 128}, T in {64, 128} (fp32 MFMA, fp32 softmax) for every call except
  * pbsa_attn_bwd, which is bf16 only (PBSA_ERR_UNSUPPORTED otherwise).
  * W <= 1024, C <= 1024, 0 <= topk <= W.
  */
@@ -166,9 +166,10 @@ int pbsa_block_mass(const pbsa_problem *p, float *mass_pool, float *mass_win, co
  * (natural log).  o: [B,H,Nq,d] in the problem dtype; lse may be NULL.
  * Workspace: optional.  With ws == NULL (or ws_bytes below
  * pbsa_workspace_size(p, PBSA_OP_FWD)) each query block runs in one
- * workgroup.  With a large enough 16-byte-aligned ws (bf16 only) and at
- * most half the GPU's resident workgroups' worth of query blocks, every
- * query block's list is cut into 2 to 8 equal ranges, one workgroup each;
+ * workgroup.  With a large enough 16-byte-aligned ws and at most half the
+ * GPU's resident workgroups' worth of query blocks, every query block's list
+ * is cut into 2 to 8 equal ranges (bf16; fp32: up to 16, at most one list
+ * entry each), one workgroup each;
  * each piece leaves a partial in ws (fp32 O, running max and row sum of
  * its 2T threads; at most 512 pieces) and a second kernel, enqueued by the
  * same call, merges them in a fixed order, so results stay bitwise

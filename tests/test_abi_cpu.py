@@ -68,8 +68,9 @@ def test_workspace_sizes():
     # and (max, sum) for each of at most 512 pieces of 256 threads
     ws_fwd = P.pbsa_workspace_size(p, P.PBSA_OP_FWD)
     assert ws_fwd >= 512 * 256 * 64 * 4 + 512 * 256 * 2 * 4
+    # the fp32 path splits the same way, with the same partial layout
     f32 = wan(); f32.dtype = P.PBSA_F32
-    assert P.pbsa_workspace_size(f32, P.PBSA_OP_FWD) == 0
+    assert P.pbsa_workspace_size(f32, P.PBSA_OP_FWD) == ws_fwd
     ws_sel = P.pbsa_workspace_size(p, P.PBSA_OP_SELECT)
     # qbar [12,37,128] f32 + per-row softmax [12,37,106] f32, 256-byte aligned
     assert ws_sel >= 12 * 37 * 128 * 4 + 12 * 37 * 106 * 4
