@@ -157,6 +157,33 @@ int pbsa_select(const pbsa_problem *p, const void *q, const pbsa_kv *kv, int32_t
                                         masses, ws, (hipStream_t)stream));
 }
 
+int pbsa_select_static(const pbsa_problem *p, const void *q, const pbsa_kv *kv, int32_t *sel,
+                       int32_t *sel_count, float *mass_pool, float *mass_win,
+                       pbsa_stream_t stream) {
+  int rc = check_problem(p, PBSA_OP_SELECT);
+  if (rc) return rc;
+  REQ(q);
+  if ((rc = check_kv_common(kv, p))) return rc;
+  REQ(kv->kbar_cur);
+  if (p->W > 0) REQ(kv->kbar_win);
+  if (p->C > 0) REQ(kv->kbar_pool);
+  if (p->topk > 0) REQ(sel);
+  REQ(sel_count);
+  const bool masses = mass_pool != nullptr || mass_win != nullptr;
+  if (masses && p->C > 0) REQ(mass_pool);
+  if (masses && p->W > 0) REQ(mass_win);
+  const size_t need = pbsa::select_ws_bytes(*p);
+  if (need > pbsa::kSelectScratchBytes)
+    return fail(PBSA_ERR_WORKSPACE,
+                "this problem needs %zu bytes of select scratch; the static scratch holds %zu "
+                "(use pbsa_select with a workspace)",
+                need, pbsa::kSelectScratchBytes);
+  return hip_status(pbsa::launch_select_static(*p, eff_scale(p), q, *kv, sel, sel_count,
+                                               masses ? mass_pool : nullptr,
+                                               masses ? mass_win : nullptr, masses,
+                                               (hipStream_t)stream));
+}
+
 int pbsa_block_mass(const pbsa_problem *p, float *mass_pool, float *mass_win, const void *ws,
                     size_t ws_bytes, pbsa_stream_t stream) {
   int rc = check_problem(p, PBSA_OP_SELECT);

@@ -12,6 +12,9 @@ namespace pbsa {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t select_ws_bytes(const pbsa_problem &p);
+// largest select workspace the allocation-free select holds (8 MiB: the
+// Wan chunk needs 0.5 MB, batch 8 of it 3.9 MB)
+constexpr size_t kSelectScratchBytes = size_t(8) << 20;
 size_t select_lds_bytes(const pbsa_problem &p);
 size_t update_ws_bytes(const pbsa_problem &p);
 size_t fwd_ws_bytes(const pbsa_problem &p);
@@ -21,6 +24,9 @@ size_t fine_ws_bytes(const pbsa_problem &p);
 hipError_t launch_select(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
                          int32_t *sel, int32_t *sel_count, float *mass_pool, float *mass_win,
                          bool masses, void *ws, hipStream_t st);
+hipError_t launch_select_static(const pbsa_problem &p, float scale, const void *q,
+                                const pbsa_kv &kv, int32_t *sel, int32_t *sel_count,
+                                float *mass_pool, float *mass_win, bool masses, hipStream_t st);
 hipError_t launch_block_mass(const pbsa_problem &p, float *mass_pool, float *mass_win,
                              const void *ws, hipStream_t st);
 hipError_t launch_block_mean(const pbsa_problem &p, const void *x, const int32_t *len,

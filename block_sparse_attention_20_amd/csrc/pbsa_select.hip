@@ -17,6 +17,8 @@
 #include "pbsa_common.h"
 #include "pbsa_internal.h"
 
+#include <mutex>
+
 namespace pbsa {
 
 // ---------------------------------------------------------------------------
@@ -381,6 +383,49 @@ hipError_t launch_select(const pbsa_problem &p, float scale, const void *q, cons
       sel_count, srows, p.H, p.d, p.T, p.W, p.C, QB, p.topk, scale, p.dev_status);
   if (masses) return launch_block_mass(p, mass_pool, mass_win, ws, st);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free select: the same launches with their workspace in a
+// file-scope device array.  Each GPU the library runs on holds its own copy
+// of the array, at its own address, until the process ends; its address on
+// a device comes from hipGetSymbolAddress with that device current (taken
+// on the first call on the device and kept).  The array's name is a host
+// stand-in and is never passed to a kernel.  Calls on one device share the
+// array, so calls that overlap in time on one device race.  Every byte the
+// kernels read is written earlier in the same call, so nothing needs
+// clearing between calls.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kSelectScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+
+static hipError_t scratch_address(void **out) {
+  static std::mutex mu;
+  static void *addr[kMaxScratchDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_select_static(const pbsa_problem &p, float scale, const void *q,
+                                const pbsa_kv &kv, int32_t *sel, int32_t *sel_count,
+                                float *mass_pool, float *mass_win, bool masses, hipStream_t st) {
+  if (select_ws_bytes(p) > kSelectScratchBytes) return hipErrorInvalidValue;
+  void *ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  return launch_select(p, scale, q, kv, sel, sel_count, mass_pool, mass_win, masses, ws, st);
 }
 
 hipError_t launch_block_mass(const pbsa_problem &p, float *mass_pool, float *mass_win,

@@ -22,7 +22,7 @@ PBSA_STATUS_POOL_COUNT, PBSA_STATUS_WIN_LEN, PBSA_STATUS_SEL, PBSA_STATUS_SINK =
 PBSA_STATUS_SHARED = 16
 
 # every exported symbol declared in include/pbsa.h
-EXPORTS = ("pbsa_select", "pbsa_block_mass", "pbsa_attn_fwd", "pbsa_attn_bwd", "pbsa_memory_update",
+EXPORTS = ("pbsa_select", "pbsa_select_static", "pbsa_block_mass", "pbsa_attn_fwd", "pbsa_attn_bwd", "pbsa_memory_update",
            "pbsa_fine_mass", "pbsa_memory_update_shared", "pbsa_block_gather", "pbsa_grad_scatter",
            "pbsa_block_mean", "pbsa_window_append", "pbsa_workspace_size", "pbsa_validate",
            "pbsa_strerror", "pbsa_last_error")
@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
         P, K, G = ctypes.POINTER(Problem), ctypes.POINTER(KV), ctypes.POINTER(KVGrad)
         sig = {
             "pbsa_select": (ctypes.c_int, [P, vp, K, vp, vp, vp, vp, vp, sz, vp]),
+            "pbsa_select_static": (ctypes.c_int, [P, vp, K, vp, vp, vp, vp, vp]),
             "pbsa_block_mass": (ctypes.c_int, [P, vp, vp, vp, sz, vp]),
             "pbsa_attn_fwd": (ctypes.c_int, [P, vp, K, vp, vp, vp, vp, vp, sz, vp]),
             "pbsa_attn_bwd": (ctypes.c_int, [P, vp, K, vp, vp, vp, vp, vp, vp, G, vp, sz, vp]),
@@ -139,6 +140,11 @@ def pbsa_select(prob, q, kv: KV, sel, sel_count, mass_pool, mass_win, ws, stream
     _check(lib().pbsa_select(ctypes.byref(prob), _p(q), ctypes.byref(kv), _p(sel), _p(sel_count),
                              _p(mass_pool), _p(mass_win), _p(ws),
                              0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def pbsa_select_static(prob, q, kv: KV, sel, sel_count, mass_pool, mass_win, stream=None):
+    _check(lib().pbsa_select_static(ctypes.byref(prob), _p(q), ctypes.byref(kv), _p(sel),
+                                    _p(sel_count), _p(mass_pool), _p(mass_win), _stream(stream)))
 
 
 def pbsa_attn_fwd(prob, q, kv: KV, sel, sel_count, o, lse, ws=None, stream=None):

@@ -146,6 +146,23 @@ int pbsa_select(const pbsa_problem *p, const void *q, const pbsa_kv *kv, int32_t
                 size_t ws_bytes, pbsa_stream_t stream);
 
 /*
+ * pbsa_select_static - pbsa_select for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and results, with the workspace taken
+ * from a static device array of 8 MiB that the library holds on each GPU it
+ * runs on until the process ends.  The caller passes inputs and outputs as
+ * for pbsa_select; nothing is allocated and nothing needs clearing.
+ * Problems whose select workspace (pbsa_workspace_size(p, PBSA_OP_SELECT))
+ * exceeds 8 MiB are refused with PBSA_ERR_WORKSPACE before any launch.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in
+ * time on one GPU (several streams or threads) race, and pbsa_block_mass
+ * cannot read the scores this call leaves (it takes a workspace).
+ */
+int pbsa_select_static(const pbsa_problem *p, const void *q, const pbsa_kv *kv, int32_t *sel,
+                       int32_t *sel_count, float *mass_pool, float *mass_win,
+                       pbsa_stream_t stream);
+
+/*
  * pbsa_block_mass - the block masses of pbsa_select (same definition and
  * section) from the coarse scores the last pbsa_select call left in ws
  * (same problem, ws untouched since), so that a rollout can take them off

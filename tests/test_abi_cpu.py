@@ -111,6 +111,13 @@ def test_entry_points_reject_before_launch():
     assert L.pbsa_select(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, fake, None, 0, None) == -5
     need = L.pbsa_workspace_size(ctypes.byref(p), P.PBSA_OP_SELECT)
     assert L.pbsa_select(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, fake, fake, need - 1, None) == -5
+    # allocation-free select: same checks, and problems whose select
+    # workspace exceeds the static scratch are refused before any launch
+    assert L.pbsa_select_static(ctypes.byref(p), fake, ctypes.byref(kv2), fake, None, fake, fake, None) == -1
+    big = P.problem(1, 256, 128, 128, 128 * 64, 0, 64, 0, P.PBSA_BF16)
+    assert L.pbsa_workspace_size(ctypes.byref(big), P.PBSA_OP_SELECT) > 8 << 20
+    assert L.pbsa_select_static(ctypes.byref(big), fake, ctypes.byref(kv2), None, fake, fake, None, None) == -5
+    assert "static scratch" in L.pbsa_last_error().decode()
     # update: n_leave out of range, negative n_sink
     assert L.pbsa_memory_update(ctypes.byref(p), ctypes.byref(kv2), fake, fake, fake, 75, 0, fake, 1 << 20, None) == -2
     assert L.pbsa_memory_update(ctypes.byref(p), ctypes.byref(kv2), fake, fake, fake, 37, -1, fake, 1 << 20, None) == -2
