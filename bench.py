@@ -432,18 +432,22 @@ def mass_compare(torch, n_chunks=16, n_layers=2, device="cuda"):
         # layer 0's pool as this chunk attends it (before this chunk's update)
         pools = {m: (ro.layers[0].t["pool_id"].clone(), ro.layers[0].t["pool_count"].clone())
                  for m, ro in ros.items()}
-        ms = {}
+        ms, fwd_ms = {}, {}
         for m, ro in ros.items():
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(n_layers)]
             e0.record()
             for l in range(n_layers):
-                ro.run_layer(l)
+                ro.run_layer(l, fwd_events=fe[l])
             e1.record()
             ro.sync_side()
             torch.cuda.synchronize()
             ms[m] = e0.elapsed_time(e1)
+            fwd_ms[m] = sum(a.elapsed_time(b) for a, b in fe)
         row = {"chunk": t, "ms_coarse": round(ms["coarse"], 3), "ms_fine": round(ms["fine"], 3),
-               "ms_shared": round(ms["shared"], 3)}
+               "ms_shared": round(ms["shared"], 3), "fwd_ms_coarse": round(fwd_ms["coarse"], 3),
+               "fwd_ms_fine": round(fwd_ms["fine"], 3)}
         # pool overlap after this chunk's update
         jac = []
         for l in range(n_layers):
@@ -483,17 +487,28 @@ def mass_compare(torch, n_chunks=16, n_layers=2, device="cuda"):
         rows.append(row)
         for ro in ros.values():
             ro.advance()
-    # pbsa_fine_mass alone on layer 0 of the fine rollout (last chunk's state)
+    # on layer 0 of the fine rollout (last chunk's state, pool of 64): the
+    # separate exact-mass pass alone, and the forward with and without the
+    # fused exact mass (pbsa_attn_fwd_mass vs pbsa_attn_fwd)
     L = ros["fine"].layers[0]
-    L.fine_mass(); torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(20):
-        L.fine_mass()
-    e1.record(); torch.cuda.synchronize()
+
+    def per_call_us(fn, n=20):
+        fn(); torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record(); torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) * 1e3 / n, 1)
+
+    fine_us = per_call_us(L.fine_mass)
+    fwd_us = per_call_us(L.fwd)
+    fwd_mass_us = per_call_us(L.fwd_mass)
     return {"workload": f"streaming rollout, {n_chunks} chunks x {n_layers} layers, pool cap {C}, "
                         "coarse vs exact block mass as the Top-C score, and a head-shared pool",
-            "per_chunk": rows, "fine_mass_us": round(e0.elapsed_time(e1) * 1e3 / 20, 1)}
+            "per_chunk": rows, "fine_mass_us": fine_us, "fwd_us": fwd_us,
+            "fwd_mass_us": fwd_mass_us,
+            "fused_mass_extra_frac": round((fwd_mass_us - fwd_us) / fwd_us, 4)}
 
 
 def train_rollout_bench(torch, n_chunks=8, device="cuda"):

@@ -119,7 +119,7 @@ const char *pbsa_strerror(int status) {
 }
 
 int pbsa_validate(const pbsa_problem *p, int op) {
-  if (op < PBSA_OP_SELECT || op > PBSA_OP_FINE_MASS) return fail(PBSA_ERR_SHAPE, "unknown op %d", op);
+  if (op < PBSA_OP_SELECT || op > PBSA_OP_FWD_MASS) return fail(PBSA_ERR_SHAPE, "unknown op %d", op);
   int rc = check_problem(p, op);
   return rc ? rc : ok();
 }
@@ -132,6 +132,7 @@ size_t pbsa_workspace_size(const pbsa_problem *p, int op) {
     case PBSA_OP_BWD: return pbsa::bwd_ws_bytes(*p);
     case PBSA_OP_UPDATE: return pbsa::update_ws_bytes(*p);
     case PBSA_OP_FINE_MASS: return pbsa::fine_ws_bytes(*p);
+    case PBSA_OP_FWD_MASS: return pbsa::fwd_mass_ws_bytes(*p);
     default: return 0;
   }
 }
@@ -256,6 +257,26 @@ int pbsa_fine_mass(const pbsa_problem *p, const void *q, const pbsa_kv *kv, cons
   if ((rc = check_ws(p, PBSA_OP_FINE_MASS, ws, ws_bytes))) return rc;
   return hip_status(pbsa::launch_fine_mass(*p, eff_scale(p), q, *kv, sel, sel_count, lse, mass_pool,
                                            mass_win, ws, (hipStream_t)stream));
+}
+
+int pbsa_attn_fwd_mass(const pbsa_problem *p, const void *q, const pbsa_kv *kv,
+                       const int32_t *sel, const int32_t *sel_count, void *o, float *lse,
+                       float *mass_pool, float *mass_win, void *ws, size_t ws_bytes,
+                       pbsa_stream_t stream) {
+  int rc = check_problem(p, PBSA_OP_FWD_MASS);
+  if (rc) return rc;
+  REQ(q);
+  if ((rc = check_kv_common(kv, p))) return rc;
+  if (p->topk > 0) REQ(sel);
+  REQ(sel_count);
+  REQ(o);
+  REQ(lse);
+  if (p->C > 0) REQ(mass_pool);
+  if (p->W > 0) REQ(mass_win);
+  if ((rc = check_ws(p, PBSA_OP_FWD_MASS, ws, ws_bytes))) return rc;
+  return hip_status(pbsa::launch_attn_fwd_mass(*p, eff_scale(p), q, *kv, sel, sel_count, o, lse,
+                                               mass_pool, mass_win, ws, ws_bytes,
+                                               (hipStream_t)stream));
 }
 
 static int memory_update_impl(const pbsa_problem *p, const pbsa_kv *kv, const float *mass_pool,

@@ -62,6 +62,12 @@ struct FwdArgs {
   int split, NB, G;
   int P;  // pieces per query block in the split launch
   float *part_o, *part_ml;
+  // exact block mass (the MASS kernels): for every query row r and scored
+  // list entry j (pool slots and selected window slots), the block's
+  // log2-sum-exp log2 sum_{u in j} 2^(s_ru scale log2 e), absolute (not
+  // relative to a running max), at blse[((item * E) + j) * BT + row]
+  float *blse;
+  int E;  // C + topk entries per item
 };
 
 __device__ __forceinline__ void item_of_block(const FwdArgs &a, int &item) {
@@ -101,7 +107,13 @@ __device__ __forceinline__ float half_swap_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <int D, int BT>
+// x over lanes l and l ^ 32, summed
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, int BT, bool MASS>
 __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh, uint16_t *K0,
                                             uint16_t *K1, uint16_t *V0, uint16_t *V1, int wg, int item,
                                             int j0, int j1) {
@@ -145,6 +157,12 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
   // that the adds of a tile are not one dependent chain
   float m = -INFINITY, l4[4] = {0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.sl2;
+  // MASS: the row sum (both lane halves, relative to m) when the previous
+  // block ended; a block's own sum is the difference.  Pool and window
+  // entries come first in the list, so the sum is still small there and the
+  // difference loses little.
+  float lprev = 0.f;
+  const int n_scored = n_pool + sc;
 
   // Per-lane LDS element offsets, fixed for the whole kernel.
   // K fragment (A of S^T): tile row tt*32 + l32, logical chunk 2kk + g.
@@ -279,6 +297,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
       const float mnew = fmaxf(m, mx);
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // m = -inf -> 0
       m = mnew;
+      if constexpr (MASS) lprev *= alpha;
 #pragma unroll
       for (int k = 0; k < 4; ++k) l4[k] *= alpha;
 #pragma unroll
@@ -319,6 +338,16 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
       }
     }
     __builtin_amdgcn_s_setprio(0);
+    if constexpr (MASS) {
+      // this tile ends block j: its log2-sum-exp for this lane's row
+      if (jn != j && j < n_scored) {
+        const float ls = half_swap_sum((l4[0] + l4[1]) + (l4[2] + l4[3]));
+        const float bs = ls - lprev;
+        lprev = ls;
+        if (g == 0 && qrow < a.Nq)
+          a.blse[((size_t)item * a.E + j) * BT + wave * 32 + l32] = bs > 0.f ? m + __log2f(bs) : -INFINITY;
+      }
+    }
     if (!more) return false;
     j = jn;
     h = hn;
@@ -370,7 +399,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
   }
 }
 
-template <int D, int BT>
+template <int D, int BT, bool MASS>
 __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   __shared__ FwdLds<D, BT> sh;
   __shared__ __attribute__((aligned(1024))) uint16_t K0[kTile * D], K1[kTile * D];
@@ -378,12 +407,13 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kerne
   int wg;
   item_of_block(a, wg);
   if (!a.split) {
-    if (wg < a.n_items) fwd_segment<D, BT>(a, sh, K0, K1, V0, V1, wg, wg, 0, a.NB);
+    if (wg < a.n_items) fwd_segment<D, BT, MASS>(a, sh, K0, K1, V0, V1, wg, wg, 0, a.NB);
     return;
   }
   if (wg >= a.G) return;
   const int pc = wg / a.n_items;
-  fwd_segment<D, BT>(a, sh, K0, K1, V0, V1, wg, wg % a.n_items, piece_start(a, pc), piece_start(a, pc + 1));
+  fwd_segment<D, BT, MASS>(a, sh, K0, K1, V0, V1, wg, wg % a.n_items, piece_start(a, pc),
+                           piece_start(a, pc + 1));
 }
 
 // Merge of the split pieces, one workgroup per (query block, 32 of the d
@@ -458,7 +488,7 @@ __global__ __launch_bounds__(2 * BT) void attn_fwd_merge_kernel(FwdArgs a) {
 //     between lanes: the exponential of element s is the B operand as is;
 //   - K and V go through LDS in 64-token tiles with padded rows (K: D + 4,
 //     V: D + 8 floats), which makes both read patterns bank-conflict free.
-template <int D, int BT>
+template <int D, int BT, bool MASS>
 __device__ __forceinline__ void fwd_f32_segment(const FwdArgs &a, float *Ks, float *Vs, int wg,
                                                 int item, int j0, int j1) {
   constexpr int NT = 2 * BT, TT = 64;
@@ -495,6 +525,7 @@ __device__ __forceinline__ void fwd_f32_segment(const FwdArgs &a, float *Ks, flo
     const float *kp, *vp;
     int len;
     resolve_block<float, D, BT>(a, bh, i, n_pool, sc, j, kp, vp, len);
+    float bsum = 0.f;  // MASS: this block's sum of P (this lane's tokens, relative to m)
     for (int h0 = 0; h0 < len; h0 += TT) {
       const int tlen = min(TT, len - h0);
       __syncthreads();  // every wave is done with the previous tile
@@ -540,6 +571,7 @@ __device__ __forceinline__ void fwd_f32_segment(const FwdArgs &a, float *Ks, flo
       const float alpha = __builtin_amdgcn_exp2f(m - muse);  // m = -inf -> 0
       m = mnew;
       l *= alpha;
+      if constexpr (MASS) bsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -551,12 +583,20 @@ __device__ __forceinline__ void fwd_f32_segment(const FwdArgs &a, float *Ks, flo
         for (int s = 0; s < 16; ++s) {
           const float p = __builtin_amdgcn_exp2f(sacc[tt][s] * sl2 - muse);
           l += p;
+          if constexpr (MASS) bsum += p;
           const int tok = tt * 32 + 8 * (s >> 2) + 4 * g + (s & 3);
           const float *vr = &Vs[tok * SV + l32];
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt)
             oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[dt * 32], p, oacc[dt], 0, 0, 0);
         }
+    }
+    if constexpr (MASS) {
+      if (j < n_pool + sc) {
+        const float bs = half_swap_sum(bsum);
+        if (g == 0 && qrow < a.Nq)
+          a.blse[((size_t)item * a.E + j) * BT + wave * 32 + l32] = bs > 0.f ? m + __log2f(bs) : -INFINITY;
+      }
     }
   }
   l += __shfl_xor(l, 32);
@@ -589,19 +629,98 @@ __device__ __forceinline__ void fwd_f32_segment(const FwdArgs &a, float *Ks, flo
   }
 }
 
-template <int D, int BT>
+template <int D, int BT, bool MASS>
 __global__ __launch_bounds__(2 * BT) void attn_fwd_f32_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) float Ks[64 * (D + 4)];
   __shared__ __attribute__((aligned(16))) float Vs[64 * (D + 8)];
   int wg;
   item_of_block(a, wg);
   if (!a.split) {
-    if (wg < a.n_items) fwd_f32_segment<D, BT>(a, Ks, Vs, wg, wg, 0, a.NB);
+    if (wg < a.n_items) fwd_f32_segment<D, BT, MASS>(a, Ks, Vs, wg, wg, 0, a.NB);
     return;
   }
   if (wg >= a.G) return;
   const int pc = wg / a.n_items;
-  fwd_f32_segment<D, BT>(a, Ks, Vs, wg, wg % a.n_items, piece_start(a, pc), piece_start(a, pc + 1));
+  fwd_f32_segment<D, BT, MASS>(a, Ks, Vs, wg, wg % a.n_items, piece_start(a, pc),
+                               piece_start(a, pc + 1));
+}
+
+// Exact block masses from the forward's per-(row, block) log2-sum-exp and
+// the final lse: M_j = sum over query rows r attending j of
+// 2^(blse_rj - lse_r log2 e), the attention probability the rows put on
+// block j.  One workgroup per (stored slot, b, h): pool slot c sums entry c
+// of every query block; window slot w sums, for every query block, the
+// entries at which it selected w.  Each thread sums its own (query block,
+// row) pairs in a fixed order, then a fixed tree over the threads: the
+// result is deterministic, and every output element is written (0 where no
+// row attends).  grid (B*H, C + W), 256 threads.
+template <int BT>
+__global__ __launch_bounds__(256) void fwd_mass_reduce_kernel(FwdArgs a, float *mass_pool,
+                                                              float *mass_win) {
+  constexpr int QPP = 256 / BT;  // query blocks per pass
+  __shared__ int first[256], count[256];
+  __shared__ float red[256];
+  const size_t bh = blockIdx.x;
+  const int slot = blockIdx.y;
+  const int t = threadIdx.x;
+  int n_pool = a.pool_count[bh];
+  n_pool = max(0, min(n_pool, a.C));
+  const bool is_pool = slot < a.C;
+  const int w = slot - a.C;
+  float acc = 0.f;
+  if (!is_pool || slot < n_pool) {
+    for (int i0 = 0; i0 < a.QB; i0 += 256) {
+      // matching list entries of query blocks i0 .. i0 + 255
+      if (i0 + t < a.QB) {
+        const int i = i0 + t;
+        int f = -1, c = 0;
+        if (is_pool) {
+          f = slot;
+          c = 1;
+        } else {
+          const int sc = max(0, min(a.sel_count[bh * a.QB + i], a.topk));
+          const int32_t *sl = a.sel + (bh * a.QB + i) * (size_t)a.topk;
+          for (int e = 0; e < sc; ++e)
+            if (sl[e] == w) {
+              if (c == 0) f = n_pool + e;
+              ++c;
+            }
+        }
+        first[t] = f;
+        count[t] = c;
+      }
+      __syncthreads();
+      const int ni = min(256, a.QB - i0);
+      for (int il = t / BT; il < ni; il += QPP) {
+        const int i = i0 + il, r = t % BT;
+        if (count[il] == 0 || i * BT + r >= a.Nq) continue;
+        const float L2 = a.lse[bh * a.Nq + (size_t)i * BT + r] * kLog2e;
+        const float *bl = a.blse + (((bh * a.QB + i) * (size_t)a.E) * BT) + r;
+        if (count[il] == 1) {
+          acc += exp2f(bl[(size_t)first[il] * BT] - L2);
+        } else {  // a slot listed more than once is attended once per listing
+          const int32_t *sl = a.sel + (bh * a.QB + i) * (size_t)a.topk;
+          const int sc = max(0, min(a.sel_count[bh * a.QB + i], a.topk));
+          for (int e = 0; e < sc; ++e)
+            if (sl[e] == w) acc += exp2f(bl[(size_t)(n_pool + e) * BT] - L2);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  red[t] = acc;
+  __syncthreads();
+#pragma unroll
+  for (int off = 128; off > 0; off >>= 1) {
+    if (t < off) red[t] += red[t + off];
+    __syncthreads();
+  }
+  if (t == 0) {
+    if (is_pool)
+      mass_pool[bh * a.C + slot] = red[0];
+    else
+      mass_win[bh * a.W + w] = red[0];
+  }
 }
 
 // Resident workgroups of the split launch: two per CU (LDS and VGPR
@@ -646,9 +765,45 @@ size_t fwd_ws_bytes(const pbsa_problem &p) {
   return split_part_o_bytes(p) + split_part_ml_bytes(p);
 }
 
+static size_t blse_bytes(const pbsa_problem &p) {
+  const size_t QB = (p.Nq + p.T - 1) / p.T;
+  const size_t E = (size_t)p.C + p.topk > 0 ? (size_t)p.C + p.topk : 1;
+  return align256((size_t)p.B * p.H * QB * E * p.T * sizeof(float));
+}
+
+static hipError_t launch_attn_fwd_impl(const pbsa_problem &p, float scale, const void *q,
+                                       const pbsa_kv &kv, const int32_t *sel,
+                                       const int32_t *sel_count, void *o, float *lse, void *ws,
+                                       size_t ws_bytes, float *blse, float *mass_pool,
+                                       float *mass_win, hipStream_t st);
+
+// the block log2-sum-exps first, then the split workspace
+size_t fwd_mass_ws_bytes(const pbsa_problem &p) { return blse_bytes(p) + fwd_ws_bytes(p); }
+
+hipError_t launch_attn_fwd_mass(const pbsa_problem &p, float scale, const void *q,
+                                const pbsa_kv &kv, const int32_t *sel, const int32_t *sel_count,
+                                void *o, float *lse, float *mass_pool, float *mass_win, void *ws,
+                                size_t ws_bytes, hipStream_t st) {
+  char *w = reinterpret_cast<char *>(ws);
+  const size_t nb = blse_bytes(p);
+  return launch_attn_fwd_impl(p, scale, q, kv, sel, sel_count, o, lse, w + nb, ws_bytes - nb,
+                              reinterpret_cast<float *>(w), mass_pool, mass_win, st);
+}
+
 hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
                            const int32_t *sel, const int32_t *sel_count, void *o, float *lse,
                            void *ws, size_t ws_bytes, hipStream_t st) {
+  return launch_attn_fwd_impl(p, scale, q, kv, sel, sel_count, o, lse, ws, ws_bytes, nullptr,
+                              nullptr, nullptr, st);
+}
+
+// blse == nullptr: plain forward; else the MASS kernels and the reduce into
+// mass_pool / mass_win (lse required)
+static hipError_t launch_attn_fwd_impl(const pbsa_problem &p, float scale, const void *q,
+                                       const pbsa_kv &kv, const int32_t *sel,
+                                       const int32_t *sel_count, void *o, float *lse, void *ws,
+                                       size_t ws_bytes, float *blse, float *mass_pool,
+                                       float *mass_win, hipStream_t st) {
   FwdArgs a;
   a.q = q;
   a.k_cur = kv.k_cur; a.v_cur = kv.v_cur; a.k_win = kv.k_win; a.v_win = kv.v_win;
@@ -664,6 +819,8 @@ hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, co
   a.G = 0;
   a.P = 1;
   a.part_o = a.part_ml = nullptr;
+  a.blse = blse;
+  a.E = p.C + p.topk > 0 ? p.C + p.topk : 1;
   int n_wg = a.n_items;
   const int64_t slots = split_slots();
   // The split pays off only when one workgroup per query block would leave
@@ -686,12 +843,18 @@ hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, co
   a.per_xcd = (n_wg + 7) / 8;
   const dim3 grid(8 * a.per_xcd);
   const dim3 block(2 * p.T);
-#define PBSA_FWD_CASE(DT, TOUT, D_, T_, KERN)                                              \
-  if (p.dtype == DT && p.d == D_ && p.T == T_) {                                           \
-    KERN<D_, T_><<<grid, block, 0, st>>>(a);                                               \
-    if (a.split)                                                                           \
-      attn_fwd_merge_kernel<D_, T_, TOUT><<<dim3(a.n_items * (D_ / 32)), block, 0, st>>>(a); \
-    return hipGetLastError();                                                              \
+#define PBSA_FWD_CASE(DT, TOUT, D_, T_, KERN)                                                \
+  if (p.dtype == DT && p.d == D_ && p.T == T_) {                                             \
+    if (blse)                                                                                \
+      KERN<D_, T_, true><<<grid, block, 0, st>>>(a);                                         \
+    else                                                                                     \
+      KERN<D_, T_, false><<<grid, block, 0, st>>>(a);                                        \
+    if (a.split)                                                                             \
+      attn_fwd_merge_kernel<D_, T_, TOUT><<<dim3(a.n_items * (D_ / 32)), block, 0, st>>>(a);   \
+    if (blse && p.C + p.W > 0)                                                               \
+      fwd_mass_reduce_kernel<T_><<<dim3(p.B * p.H, p.C + p.W), 256, 0, st>>>(a, mass_pool,   \
+                                                                             mass_win);      \
+    return hipGetLastError();                                                                \
   }
   PBSA_FWD_CASE(PBSA_BF16, uint16_t, 128, 128, attn_fwd_bf16_kernel)
   PBSA_FWD_CASE(PBSA_BF16, uint16_t, 64, 128, attn_fwd_bf16_kernel)

@@ -18,6 +18,7 @@ constexpr size_t kSelectScratchBytes = size_t(8) << 20;
 size_t select_lds_bytes(const pbsa_problem &p);
 size_t update_ws_bytes(const pbsa_problem &p);
 size_t fwd_ws_bytes(const pbsa_problem &p);
+size_t fwd_mass_ws_bytes(const pbsa_problem &p);
 size_t bwd_ws_bytes(const pbsa_problem &p);
 size_t fine_ws_bytes(const pbsa_problem &p);
 
@@ -37,6 +38,10 @@ hipError_t launch_window_append(const pbsa_problem &p, const pbsa_kv &kv, void *
 hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
                            const int32_t *sel, const int32_t *sel_count, void *o, float *lse,
                            void *ws, size_t ws_bytes, hipStream_t st);
+hipError_t launch_attn_fwd_mass(const pbsa_problem &p, float scale, const void *q,
+                                const pbsa_kv &kv, const int32_t *sel, const int32_t *sel_count,
+                                void *o, float *lse, float *mass_pool, float *mass_win, void *ws,
+                                size_t ws_bytes, hipStream_t st);
 hipError_t launch_attn_bwd(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
                            const int32_t *sel, const int32_t *sel_count, const void *o,
                            const float *lse, const void *dout, void *dq, const pbsa_kv_grad &g,

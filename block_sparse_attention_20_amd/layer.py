@@ -58,6 +58,7 @@ class PBSALayer:
         # run one after another on one stream can share it)
         self.ws_fwd = P.workspace(self.prob, P.PBSA_OP_FWD, device) if isinstance(ws_fwd, str) else ws_fwd
         self.ws_fine = None  # allocated on first use of fine_mass()
+        self.ws_fwd_mass = None  # allocated on first use of fwd_mass() (or shared, set by the owner)
         self._kv = None
 
     # -- state ---------------------------------------------------------------
@@ -115,6 +116,16 @@ class PBSALayer:
         t = self.t
         P.pbsa_attn_fwd(self.prob, t["q"], self.kv, t["sel"] if self.topk > 0 else None,
                         t["sel_count"], t["o"], t["lse"] if with_lse else None, self.ws_fwd)
+
+    def fwd_mass(self):
+        """Forward plus the exact block masses from the forward's own walk
+        (pbsa_attn_fwd_mass) into mass_pool / mass_win."""
+        t = self.t
+        if self.ws_fwd_mass is None:
+            self.ws_fwd_mass = P.workspace(self.prob, P.PBSA_OP_FWD_MASS, self.device)
+        P.pbsa_attn_fwd_mass(self.prob, t["q"], self.kv, t["sel"] if self.topk > 0 else None,
+                             t["sel_count"], t["o"], t["lse"], t["mass_pool"] if self.C > 0 else None,
+                             t["mass_win"] if self.W > 0 else None, self.ws_fwd_mass)
 
     def bwd(self, dout: torch.Tensor, grads: Optional[dict] = None) -> dict:
         t = self.t

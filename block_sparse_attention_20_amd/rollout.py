@@ -20,7 +20,8 @@ The state of a layer is plain device tensors (``PBSALayer.t``), so it can be
 saved and restored with ``state_dict`` / ``load_state_dict``.
 
 With ``mass="fine"`` the update ranks blocks by their exact attention mass
-(pbsa_fine_mass, from the forward's lse) instead of the coarse mass; with
+instead of the coarse mass: the forward of each layer is pbsa_attn_fwd_mass,
+which records the masses during its own walk; with
 ``shared_pool=True`` all heads of a layer keep one pool, ranked by the masses
 summed over heads (pbsa_memory_update_shared).
 
@@ -38,6 +39,7 @@ from typing import List, Optional
 
 import torch
 
+from . import pbsa as P
 from .layer import PBSALayer
 
 STATE_KEYS = ("k_win", "v_win", "win_len", "win_id", "kbar_win", "k_pool", "v_pool", "pool_len",
@@ -63,6 +65,10 @@ class Rollout:
             PBSALayer(B, H, d, T, Nq, self.W, C, topk, dtype=dtype, scale=scale, device=device,
                       ws_fwd=first.ws_fwd)
             for _ in range(n_layers - 1)]
+        if mass == "fine":   # one fused forward + mass workspace for all layers (one stream)
+            ws = P.workspace(first.prob, P.PBSA_OP_FWD_MASS, device)
+            for L in self.layers:
+                L.ws_fwd_mass = ws
         self.leaving = [torch.arange(p * self.QB, (p + 1) * self.QB, dtype=torch.int32, device=device)
                         for p in range(window_chunks)]
         self.t = 0
@@ -100,7 +106,10 @@ class Rollout:
         if attention:
             if fwd_events is not None:
                 fwd_events[0].record()
-            L.fwd()
+            if self.mass == "fine" and t >= self.window_chunks:
+                L.fwd_mass()         # the update after this chunk ranks by these masses
+            else:
+                L.fwd()
             if fwd_events is not None:
                 fwd_events[1].record()
         if self.side is None:
@@ -116,7 +125,7 @@ class Rollout:
     def _side_work(self, L, t):
         if t >= self.window_chunks:
             if self.mass == "fine" and self._attended:
-                L.fine_mass()        # reads this chunk's lse
+                pass                 # pbsa_attn_fwd_mass wrote the masses
             elif self.side is not None or self.mass == "fine":
                 L.block_mass()       # coarse masses from the select scores
             L.update(self.leaving[t % self.window_chunks], self.n_sink, shared=self.shared_pool)

@@ -76,7 +76,7 @@ enum {
 };
 
 enum { PBSA_OP_SELECT = 0, PBSA_OP_FWD = 1, PBSA_OP_BWD = 2, PBSA_OP_UPDATE = 3,
-       PBSA_OP_FINE_MASS = 4 };
+       PBSA_OP_FINE_MASS = 4, PBSA_OP_FWD_MASS = 5 };
 
 /* Bits OR-ed into *dev_status by kernels (device-side metadata faults). */
 enum {
@@ -232,6 +232,24 @@ int pbsa_attn_bwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const
 int pbsa_fine_mass(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const int32_t *sel,
                    const int32_t *sel_count, const float *lse, float *mass_pool, float *mass_win,
                    void *ws, size_t ws_bytes, pbsa_stream_t stream);
+
+/*
+ * pbsa_attn_fwd_mass - pbsa_attn_fwd and the exact block masses of
+ * pbsa_fine_mass (same definitions and sections) in one call: the forward's
+ * own walk records, for every query row and every pool or selected window
+ * block it attends, the block's log-sum-exp of the row's logits, and a small
+ * kernel then forms M_j = sum_r exp(blse_rj - lse_r) with the final lse, so
+ * the masses cost no second pass over K.  o and lse as pbsa_attn_fwd (lse
+ * required here); mass_pool / mass_win as pbsa_fine_mass (required when
+ * C > 0 / W > 0, fp32, written in full, deterministic).
+ * Workspace: pbsa_workspace_size(p, PBSA_OP_FWD_MASS) bytes, required (the
+ * per-row block log-sum-exps, then the forward's split workspace); no
+ * initialisation needed; calls that share one ws must not overlap in time.
+ */
+int pbsa_attn_fwd_mass(const pbsa_problem *p, const void *q, const pbsa_kv *kv,
+                       const int32_t *sel, const int32_t *sel_count, void *o, float *lse,
+                       float *mass_pool, float *mass_win, void *ws, size_t ws_bytes,
+                       pbsa_stream_t stream);
 
 /*
  * pbsa_memory_update - Top-C retention of the persistent pool ("Arquitectura

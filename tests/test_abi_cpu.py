@@ -80,7 +80,11 @@ def test_workspace_sizes():
     # fine mass: one fp32 partial sum per (b, h, query block, wave slot, entry)
     assert P.pbsa_workspace_size(p, P.PBSA_OP_FINE_MASS) >= 12 * 37 * 4 * (32 + 16) * 4
     assert P.pbsa_validate(p, P.PBSA_OP_FINE_MASS) == 0
-    assert P.pbsa_validate(p, P.PBSA_OP_FINE_MASS + 1) == -2
+    assert P.pbsa_validate(p, P.PBSA_OP_FWD_MASS) == 0
+    assert P.pbsa_validate(p, P.PBSA_OP_FWD_MASS + 1) == -2
+    # fused forward + exact mass: one log-sum-exp per (row, scored entry), then
+    # the forward's split workspace
+    assert P.pbsa_workspace_size(p, P.PBSA_OP_FWD_MASS) >= 12 * 37 * 48 * 128 * 4 + ws_fwd
 
 
 def test_entry_points_reject_before_launch():
@@ -135,6 +139,16 @@ def test_entry_points_reject_before_launch():
                             need, None) == -1
     assert L.pbsa_fine_mass(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, fake, fake, fake,
                             need - 1, None) == -5
+    # fused forward + mass: lse, both mass buffers and the workspace required
+    need = L.pbsa_workspace_size(ctypes.byref(p), P.PBSA_OP_FWD_MASS)
+    assert L.pbsa_attn_fwd_mass(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, None, fake,
+                                fake, fake, need, None) == -1
+    assert L.pbsa_attn_fwd_mass(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, fake, None,
+                                fake, fake, need, None) == -1
+    assert L.pbsa_attn_fwd_mass(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, fake, fake,
+                                fake, fake, need - 1, None) == -5
+    assert L.pbsa_attn_fwd_mass(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, fake, fake,
+                                fake, None, 0, None) == -5
     # gather / scatter: slot counts, id strides, chunk counts, required pointers
     assert L.pbsa_block_gather(ctypes.byref(p), fake, 0, None, 70000, fake, fake, 2, fake, fake, None, None) == -2
     assert L.pbsa_block_gather(ctypes.byref(p), fake, 3, None, 4, fake, fake, 2, fake, fake, None, None) == -2

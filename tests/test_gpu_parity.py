@@ -200,6 +200,93 @@ def test_fine_mass_matches_oracle(name):
     assert L.status_bits() == 0
 
 
+@pytest.mark.parametrize("name", ["bf16_d128_T128_small", "bf16_d64_T64_multi", "bf16_d64_T128",
+                                  "bf16_d128_T64", "f32_d64_T64", "f32_d128_T128",
+                                  "empty_pool_and_window", "topk_covers_window", "long_list",
+                                  "long_list_d128_T128", "current_only"])
+def test_fwd_mass_matches_oracle(name):
+    """The fused forward + exact block mass (pbsa_attn_fwd_mass): O and LSE
+    as the plain forward (oracle bars), masses against the oracle's exact
+    mass on the GPU's own selection (5e-3 of the largest mass for bf16, 5e-5
+    for fp32, blocks no row attends exactly 0) and against the separate
+    exact-mass pass (pbsa_fine_mass) to 1e-4 of the largest mass."""
+    shape, kw = CASES[name]
+    _log(f"fused fwd + mass case {name}")
+    st = syn.make_state(shape, 13, pad_value=float("nan"), **kw)
+    L = run(shape, st)
+    L.fine_mass()
+    torch.cuda.synchronize()
+    sep = {n: L.t[n].clone() for n in ("mass_pool", "mass_win")}
+    for n in ("mass_pool", "mass_win", "o", "lse"):
+        L.t[n].fill_(float("nan"))
+    L.fwd_mass()
+    torch.cuda.synchronize()
+    scale = eff_scale(shape, 0.0)
+    gsel = L.t["sel"].cpu().numpy(); gcnt = L.t["sel_count"].cpu().numpy()
+    f = po.attn_fwd(st, gsel, gcnt, scale, shape.T)
+    o = L.t["o"].float().cpu().numpy(); lse = L.t["lse"].cpu().numpy()
+    if shape.dtype == torch.float32:
+        assert np.abs(o - f["o"]).max() <= 1e-4
+        assert np.abs(lse - f["lse"]).max() <= 1e-5
+    else:
+        check_close_bf16(o, f["o"], f"{name} fused")
+        assert np.abs(lse - f["lse"]).max() <= 2e-3
+    ref = po.fine_mass(st, gsel, gcnt, scale, shape.T)
+    rtol = 5e-5 if shape.dtype == torch.float32 else 5e-3
+    for n, C in (("mass_pool", shape.C), ("mass_win", shape.W)):
+        if C == 0:
+            continue
+        got = L.t[n].cpu().numpy()[..., :C]
+        r = ref[n]
+        assert not np.isnan(got).any(), f"{name}: {n} not fully written"
+        top = max(np.abs(r).max(), 1e-30)
+        err = np.abs(got - r).max()
+        _log(f"{name} fused {n}: max-abs {err:.3e} (bar {rtol * top + 1e-7:.3e})")
+        assert err <= rtol * top + 1e-7, (name, n, err)
+        assert (got[r == 0] == 0).all(), f"{name}: {n} nonzero where no row attends"
+        d_sep = np.abs(got - sep[n].cpu().numpy()[..., :C]).max()
+        assert d_sep <= 1e-4 * top + 1e-7, (name, n, "vs pbsa_fine_mass", d_sep)
+    assert L.status_bits() == 0
+
+
+@pytest.mark.parametrize("unscaled", [False, True])
+def test_fwd_mass_wan_chunk_full_size(unscaled):
+    """The fused forward + exact mass at the Wan chunk, full size, in the
+    benchmark's launch configuration: O and LSE equal to the plain forward's
+    within rounding, two heads' masses against the oracle, every head's
+    against the separate exact-mass pass."""
+    _log(f"fused fwd + mass, wan chunk unscaled={unscaled}")
+    shape = syn.WAN_CHUNK
+    st = syn.wan_chunk_state(0, unscaled=unscaled)
+    L = run(shape, st)
+    o_plain = L.t["o"].float().cpu().numpy(); lse_plain = L.t["lse"].cpu().numpy()
+    L.fine_mass()
+    torch.cuda.synchronize()
+    sep = {n: L.t[n].cpu().numpy() for n in ("mass_pool", "mass_win")}
+    for n in ("mass_pool", "mass_win", "o", "lse"):
+        L.t[n].fill_(float("nan"))
+    L.fwd_mass()
+    torch.cuda.synchronize()
+    o = L.t["o"].float().cpu().numpy(); lse = L.t["lse"].cpu().numpy()
+    assert np.abs(lse - lse_plain).max() <= 1e-5
+    assert np.abs(o - o_plain).max() <= 1e-2 * np.abs(o_plain).max()
+    mp = L.t["mass_pool"].cpu().numpy(); mw = L.t["mass_win"].cpu().numpy()
+    for n, got in (("mass_pool", mp), ("mass_win", mw)):
+        top = np.abs(sep[n]).max()
+        assert np.abs(got - sep[n]).max() <= 1e-4 * top, n
+    gsel = L.t["sel"].cpu().numpy(); gcnt = L.t["sel_count"].cpu().numpy()
+    scale = 1 / math.sqrt(128)
+    for h in (0, 7):
+        ref = po.fine_mass(_one_head(st, h), gsel[:, h:h + 1], gcnt[:, h:h + 1], scale, shape.T)
+        for n, got in (("mass_pool", mp[:, h:h + 1]), ("mass_win", mw[:, h:h + 1])):
+            r = ref[n]
+            err = np.abs(got - r).max()
+            bar = 5e-3 * np.abs(r).max() + 1e-7
+            _log(f"fused head {h} {n}: max-abs {err:.3e} (bar {bar:.3e})")
+            assert err <= bar, (h, n, err, bar)
+    assert L.status_bits() == 0
+
+
 @pytest.mark.parametrize("name", ["bf16_d128_T128_small", "bf16_d64_T64_multi", "bf16_d128_T64",
                                   "bf16_d64_T128", "empty_pool_and_window", "one_entry_list"])
 def test_fwd_split_and_one_block_per_workgroup_agree(name):
