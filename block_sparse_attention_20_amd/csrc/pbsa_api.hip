@@ -192,7 +192,8 @@ int pbsa_block_mass(const pbsa_problem *p, float *mass_pool, float *mass_win, co
   if (p->C > 0) REQ(mass_pool);
   if (p->W > 0) REQ(mass_win);
   if ((rc = check_ws(p, PBSA_OP_SELECT, ws, ws_bytes))) return rc;
-  return hip_status(pbsa::launch_block_mass(*p, mass_pool, mass_win, ws, (hipStream_t)stream));
+  return hip_status(pbsa::launch_block_mass(*p, eff_scale(p), mass_pool, mass_win, ws,
+                                            (hipStream_t)stream));
 }
 
 int pbsa_attn_fwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const int32_t *sel,

@@ -11,9 +11,13 @@
 // the coarse softmax over everything the chunk sees, summed over the
 // chunk's query blocks.
 //
-// All of this is HBM/latency bound and tiny next to the attention: three
-// launches (block means; scores + top-k per query block; block mass per
-// head), each written so its global loads are in flight together.
+// All of this is HBM/latency bound and tiny next to the attention.  The
+// window top-k of a query block needs only the block's own query mean and
+// the cached pool/window representatives, so the critical path is one
+// launch per query block: its own query and key means, pool and window
+// scores, top-k.  The scores against the current chunk's blocks (whose means
+// are spread over all the query blocks' workgroups) are needed only for the
+// block masses, and are formed by the block-mass kernel, which runs later.
 #include "pbsa_common.h"
 #include "pbsa_internal.h"
 
@@ -62,21 +66,55 @@ __device__ void block_mean_wg(const TIn *__restrict__ src, int n, int d, float *
   __syncthreads();
 }
 
-// grid (QB, H, B*2): z even = Q -> qbar (workspace), z odd = K_cur -> kbar_cur.
+// Means of the first n rows of two [rows, d] blocks a and b (row stride d)
+// at once, so that both blocks' loads are in flight together; fp32 sums in
+// a fixed order.  256 threads, 16-byte loads; red: LDS, >= 2*256*8 floats.
+// Threads [0, d) write out_a[t], threads [d, 2d) out_b[t - d]; both means
+// also go to both[0, 2d) (LDS).
 template <typename TIn>
-__global__ __launch_bounds__(256) void chunk_means_kernel(const TIn *__restrict__ q,
-                                                          const TIn *__restrict__ k,
-                                                          float *__restrict__ qbar,
-                                                          float *__restrict__ kbar, int H, int Nq,
-                                                          int d, int T, int QB) {
-  __shared__ float red[256 * 8];
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z >> 1, which = blockIdx.z & 1;
-  const size_t bh = (size_t)b * H + h;
-  const int r0 = i * T;
-  const int n = min(T, Nq - r0);
-  const TIn *src = (which ? k : q) + (bh * Nq + r0) * d;
-  float *dst = (which ? kbar : qbar) + (bh * QB + i) * d;
-  block_mean_wg<TIn>(src, n, d, dst, red);
+__device__ void two_block_means(const TIn *__restrict__ a, const TIn *__restrict__ b, int n, int d,
+                                float *out_a, float *out_b, float *red, float *both) {
+  constexpr int E = 16 / sizeof(TIn);
+  const int tpr = d / E, rpp = 256 / tpr;
+  const int t = threadIdx.x;
+  const int rg = t / tpr, cg = t % tpr;
+  float acc[2][E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[0][e] = acc[1][e] = 0.f;
+#pragma unroll 8
+  for (int r = rg; r < n; r += rpp) {
+    const u32x4 va = *reinterpret_cast<const u32x4 *>(a + (size_t)r * d + cg * E);
+    const u32x4 vb = *reinterpret_cast<const u32x4 *>(b + (size_t)r * d + cg * E);
+    if constexpr (sizeof(TIn) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[0][2 * e] += bflo(va[e]);
+        acc[0][2 * e + 1] += bfhi(va[e]);
+        acc[1][2 * e] += bflo(vb[e]);
+        acc[1][2 * e + 1] += bfhi(vb[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[0][e] += __uint_as_float(va[e]);
+        acc[1][e] += __uint_as_float(vb[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    red[rg * d + cg * E + e] = acc[0][e];
+    red[256 * 8 + rg * d + cg * E + e] = acc[1][e];
+  }
+  __syncthreads();
+  if (t < 2 * d) {
+    const int c = t % d, w = t / d;
+    float s = 0.f;
+    for (int g = 0; g < rpp; ++g) s += red[w * 256 * 8 + g * d + c];
+    const float v = n > 0 ? s / (float)n : 0.f;
+    if (w == 0) out_a[c] = v; else out_b[c] = v;
+    both[t] = v;  // [a | b], for the caller (after a sync)
+  }
 }
 
 // grid (n_blocks): means of stored slot blocks [n, T, d] with lengths
@@ -96,36 +134,40 @@ __global__ __launch_bounds__(256) void slot_means_kernel(const TIn *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Coarse scores + window top-k.  grid (QB, H, B), 256 threads.
-//  - candidates [pool C | window W | current QB], 16 lanes per candidate
-//    (coalesced 16-byte reads of kbar, 4 shuffles); all of a pass's loads
-//    are issued before any is used;
-//  - the score row goes to the workspace for the block-mass kernel;
+// Own-block means, coarse scores + window top-k.  grid (QB, H, B), 256 threads.
+//  - the query block's Q rows and K rows (the current chunk's block i) are
+//    averaged together: qbar_i to LDS and to the workspace (for the block
+//    mass), kbar_cur_i to its cache;
+//  - candidates [pool C | window W], 16 lanes per candidate (coalesced
+//    16-byte reads of kbar, 4 shuffles); the first batch of candidate loads
+//    is issued before the means are reduced;
+//  - the score row's pool and window part goes to the workspace for the
+//    block-mass kernel (which adds the current-chunk part);
 //  - top-k is rank based: a valid window slot is selected iff fewer than k
 //    valid slots rank before it in the total order (score desc, id asc, NaN
 //    last); its output position is the number of selected slots below it.
 //    Exact and order-independent, hence deterministic.  Scores enter the
 //    ranking as order keys (order_key; 0 = invalid slot), so the pairwise
 //    comparisons are branch free.
-// Dynamic LDS: q[128] floats, window ids [W] int64, keys [W], flags [W],
-// ranks [W].
+// Dynamic LDS: window ids [W] int64, keys [W], flags [W], ranks [W].
 // ---------------------------------------------------------------------------
-// 16 candidates per pass; 9 passes cover the 143 candidates of the Wan
-// chunk (pool 32 + window 74 + 37 current blocks) with one batch of loads:
-// 16.3 us for means + scores + top-k there, against 18.6 us with 8 (which
-// needs a second, almost empty batch) and 16.5 us with 3 or 5.
-constexpr int kScorePasses = 9;
+// 16 candidates per pass; 7 passes cover the 106 pool and window candidates
+// of the Wan chunk (pool 32 + window 74) with one batch of loads.
+constexpr int kScorePasses = 7;
 
+template <typename TIn>
 __global__ __launch_bounds__(256) void score_topk_kernel(
-    const float *__restrict__ qbar, const float *__restrict__ kbar_pool,
-    const float *__restrict__ kbar_win, const float *__restrict__ kbar_cur,
-    const int32_t *__restrict__ pool_count, const int32_t *__restrict__ win_len,
-    const int64_t *__restrict__ win_id, int32_t *__restrict__ sel, int32_t *__restrict__ sel_count,
-    float *__restrict__ srow_out, int H, int d, int T, int W, int C, int QB, int topk, float scale,
-    int32_t *status) {
+    const TIn *__restrict__ q, const TIn *__restrict__ k_cur, float *__restrict__ qbar_out,
+    float *__restrict__ kbarc_out, float *__restrict__ kbar_cur, const float *__restrict__ kbar_pool,
+    const float *__restrict__ kbar_win, const int32_t *__restrict__ pool_count,
+    const int32_t *__restrict__ win_len, const int64_t *__restrict__ win_id,
+    int32_t *__restrict__ sel, int32_t *__restrict__ sel_count, float *__restrict__ srow_out,
+    int H, int Nq, int d, int T, int W, int C, int QB, int topk, float scale, int32_t *status) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  float *qv = smem;                                        // [128]
-  int64_t *wid = reinterpret_cast<int64_t *>(qv + 128);   // [W]
+  __shared__ __attribute__((aligned(16))) float qv[128];
+  __shared__ float red[2 * 256 * 8];
+  __shared__ float both[256];
+  int64_t *wid = reinterpret_cast<int64_t *>(smem);          // [W]
   uint32_t *key = reinterpret_cast<uint32_t *>(wid + W);  // [W]: order keys
   int *flag = reinterpret_cast<int *>(key + W);           // [W]: 1 valid, 2 selected
   int *rank = flag + W;                                    // [W]
@@ -140,7 +182,6 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
     if (t == 0) set_status(status, PBSA_STATUS_POOL_COUNT);
     n_pool = max(0, min(n_pool, C));
   }
-  if (t < d) qv[t] = qbar[(bh * QB + i) * d + t];
   int nv = 0;
   for (int w = t; w < W; w += 256) {
     const int len = win_len[w];
@@ -150,17 +191,14 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
     wid[w] = win_id[w];
   }
   if (t == 0) nvalid_sh = 0;
-  __syncthreads();
-  for (int o = 32; o > 0; o >>= 1) nv += __shfl_xor(nv, o);
-  if (lane == 0) atomicAdd(&nvalid_sh, nv);
-
-  const int nj = C + W + QB;
+  const int nj = C + W;                 // candidates scored here
+  const int nrow = C + W + QB;          // score row length (current part: block mass)
   const int sub = lane >> 4, sl = lane & 15;
   const int per = d / 16;  // floats per lane (8 or 4)
-  float *srow = srow_out + (bh * QB + i) * (size_t)nj;
-  for (int base = wave * 4; base < nj; base += 16 * kScorePasses) {
-    f32x4 k0[kScorePasses], k1[kScorePasses];
-    bool ok[kScorePasses];
+  float *srow = srow_out + (bh * QB + i) * (size_t)nrow;
+  // one batch of candidate loads (the first kScorePasses * 16 candidates)
+  auto load_batch = [&](int base, f32x4 (&k0)[kScorePasses], f32x4 (&k1)[kScorePasses],
+                        bool (&ok)[kScorePasses]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ps = 0; ps < kScorePasses; ++ps) {
       const int j = base + ps * 16 + sub;
@@ -169,12 +207,9 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
       if (j < C) {
         valid = j < n_pool;
         kb = kbar_pool + (bh * C + j) * d;
-      } else if (j < C + W) {
-        valid = flag[j - C] != 0;
-        kb = kbar_win + (bh * W + (j - C)) * d;
       } else if (j < nj) {
-        valid = true;
-        kb = kbar_cur + (bh * QB + (j - C - W)) * d;
+        valid = win_len[j - C] > 0;
+        kb = kbar_win + (bh * W + (j - C)) * d;
       }
       ok[ps] = valid;
       k0[ps] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -184,6 +219,25 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
         if (per == 8) k1[ps] = *reinterpret_cast<const f32x4 *>(kb + sl * per + 4);
       }
     }
+  };
+  f32x4 k0[kScorePasses], k1[kScorePasses];
+  bool ok[kScorePasses];
+  int base = wave * 4;
+  load_batch(base, k0, k1, ok);
+  // the block's own means (Q -> qbar, K -> kbar_cur)
+  {
+    const int r0 = i * T, n = min(T, Nq - r0);
+    two_block_means<TIn>(q + (bh * Nq + r0) * d, k_cur + (bh * Nq + r0) * d, n, d, qv,
+                         kbar_cur + (bh * QB + i) * d, red, both);
+  }
+  __syncthreads();
+  if (t < d) {
+    qbar_out[(bh * QB + i) * d + t] = qv[t];
+    kbarc_out[(bh * QB + i) * d + t] = both[d + t];
+  }
+  for (int o = 32; o > 0; o >>= 1) nv += __shfl_xor(nv, o);
+  if (lane == 0) atomicAdd(&nvalid_sh, nv);
+  for (;;) {
 #pragma unroll
     for (int ps = 0; ps < kScorePasses; ++ps) {
       const int j = base + ps * 16 + sub;
@@ -197,9 +251,12 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
       if (sl == 0 && j < nj) {
         const float v = ok[ps] ? acc * scale : -INFINITY;
         srow[j] = v;
-        if (j >= C && j < C + W) key[j - C] = ok[ps] ? order_key(v) : 0u;
+        if (j >= C) key[j - C] = ok[ps] ? order_key(v) : 0u;
       }
     }
+    base += 16 * kScorePasses;
+    if (base >= nj) break;
+    load_batch(base, k0, k1, ok);
   }
   __syncthreads();
 
@@ -261,15 +318,16 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
 constexpr int kMassLds = 12288;  // floats of staged scores
 constexpr int kMassThreads = 1024;
 
-__global__ __launch_bounds__(kMassThreads) void block_mass_kernel(const float *__restrict__ srows,
-                                                                  float *__restrict__ mass_pool,
-                                                                  float *__restrict__ mass_win,
-                                                                  int H, int W, int C, int QB) {
+__global__ __launch_bounds__(kMassThreads) void block_mass_kernel(
+    const float *__restrict__ srows, const float *__restrict__ qbar, const float *__restrict__ kbarc,
+    float *__restrict__ mass_pool, float *__restrict__ mass_win, int H, int W, int C, int QB, int d,
+    float scale) {
   __shared__ float sbuf[kMassLds];
   __shared__ float rmax[kMassThreads / 64 * 16], rinv[kMassThreads / 64 * 16];
   const size_t bh = (size_t)blockIdx.y * H + blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   constexpr int NWV = kMassThreads / 64;
+  const int sub = lane >> 4, sl = lane & 15, per = d / 16;
   const int nj = C + W + QB;
   const int rows_per = max(1, min(NWV * 16, kMassLds / nj));
   const float *src = srows + bh * QB * (size_t)nj;
@@ -278,8 +336,48 @@ __global__ __launch_bounds__(kMassThreads) void block_mass_kernel(const float *_
     const int nr = min(rows_per, QB - r0);
     __syncthreads();
     const float *s0 = src + (size_t)r0 * nj;
+    // pool and window scores from the select kernel ...
 #pragma unroll 8
-    for (int e = t; e < nr * nj; e += kMassThreads) sbuf[e] = s0[e];
+    for (int e = t; e < nr * nj; e += kMassThreads)
+      if (e % nj < C + W) sbuf[e] = s0[e];
+    // ... and the current-chunk scores s_rj = scale <qbar_r, kbar_cur_j>,
+    // 16 lanes per dot product (the select kernel's summation order).  A
+    // wave takes a row (its query mean loaded once), its four 16-lane groups
+    // columns j = sub, sub + 4, ..., with kMassU column loads in flight.
+    constexpr int kMassU = 4;
+    for (int r = wave; r < nr; r += NWV) {
+      const float *qq = qbar + (bh * QB + r0 + r) * (size_t)d + sl * per;
+      const f32x4 q0 = *reinterpret_cast<const f32x4 *>(qq);
+      f32x4 q1 = {0.f, 0.f, 0.f, 0.f};
+      if (per == 8) q1 = *reinterpret_cast<const f32x4 *>(qq + 4);
+      for (int j0 = sub; j0 < QB; j0 += 4 * kMassU) {
+        f32x4 k0[kMassU], k1[kMassU];
+#pragma unroll
+        for (int u = 0; u < kMassU; ++u) {
+          const int j = j0 + 4 * u;
+          k0[u] = k1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (j < QB) {
+            const float *kk = kbarc + (bh * QB + j) * (size_t)d + sl * per;
+            k0[u] = *reinterpret_cast<const f32x4 *>(kk);
+            if (per == 8) k1[u] = *reinterpret_cast<const f32x4 *>(kk + 4);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kMassU; ++u) {
+          const int j = j0 + 4 * u;
+          if (j < QB) {  // the same for all 16 lanes of a group
+            float acc = q0[0] * k0[u][0] + q0[1] * k0[u][1] + q0[2] * k0[u][2] + q0[3] * k0[u][3];
+            if (per == 8)
+              acc += q1[0] * k1[u][0] + q1[1] * k1[u][1] + q1[2] * k1[u][2] + q1[3] * k1[u][3];
+            acc += __shfl_xor(acc, 1);
+            acc += __shfl_xor(acc, 2);
+            acc += __shfl_xor(acc, 4);
+            acc += __shfl_xor(acc, 8);
+            if (sl == 0) sbuf[r * nj + C + W + j] = acc * scale;
+          }
+        }
+      }
+    }
     __syncthreads();
     // per-row max and 1/sum, one wave per row
     for (int r = wave; r < nr; r += NWV) {
@@ -351,37 +449,50 @@ __global__ __launch_bounds__(256) void window_append_kernel(
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
+// Select workspace: query-block means [bh][QB][d], score rows
+// [bh][QB][C + W + QB] (pool, window, current), copies of the current
+// blocks' key means [bh][QB][d] for the block-mass kernel.
 size_t select_ws_bytes(const pbsa_problem &p) {
   const size_t QB = (p.Nq + p.T - 1) / p.T;
   const size_t bh = (size_t)p.B * p.H;
-  return align256(bh * QB * p.d * sizeof(float)) +
+  return 2 * align256(bh * QB * p.d * sizeof(float)) +
          align256(bh * QB * (p.C + p.W + QB) * sizeof(float));
 }
 
+static void select_ws_layout(const pbsa_problem &p, const void *ws, float *&qbar, float *&srows,
+                             float *&kbarc) {
+  const size_t QB = (p.Nq + p.T - 1) / p.T;
+  const size_t bh = (size_t)p.B * p.H;
+  char *w = reinterpret_cast<char *>(const_cast<void *>(ws));
+  qbar = reinterpret_cast<float *>(w);
+  w += align256(bh * QB * p.d * sizeof(float));
+  srows = reinterpret_cast<float *>(w);
+  w += align256(bh * QB * (p.C + p.W + QB) * sizeof(float));
+  kbarc = reinterpret_cast<float *>(w);
+}
+
 size_t select_lds_bytes(const pbsa_problem &p) {
-  return 128 * sizeof(float) + (size_t)p.W * (sizeof(uint32_t) + 2 * sizeof(int) + sizeof(int64_t));
+  return (size_t)p.W * (sizeof(uint32_t) + 2 * sizeof(int) + sizeof(int64_t));
 }
 
 hipError_t launch_select(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
                          int32_t *sel, int32_t *sel_count, float *mass_pool, float *mass_win,
                          bool masses, void *ws, hipStream_t st) {
   const int QB = (p.Nq + p.T - 1) / p.T;
-  const size_t bh = (size_t)p.B * p.H;
-  float *qbar = reinterpret_cast<float *>(ws);
-  char *wsb = reinterpret_cast<char *>(ws);
-  float *srows = reinterpret_cast<float *>(wsb + align256(bh * QB * p.d * sizeof(float)));
-  dim3 g1(QB, p.H, p.B * 2);
+  float *qbar, *srows, *kbarc;
+  select_ws_layout(p, ws, qbar, srows, kbarc);
+  const dim3 g(QB, p.H, p.B);
   if (p.dtype == PBSA_BF16)
-    chunk_means_kernel<uint16_t><<<g1, 256, 0, st>>>(
-        (const uint16_t *)q, (const uint16_t *)kv.k_cur, qbar, kv.kbar_cur, p.H, p.Nq, p.d, p.T, QB);
+    score_topk_kernel<uint16_t><<<g, 256, select_lds_bytes(p), st>>>(
+        (const uint16_t *)q, (const uint16_t *)kv.k_cur, qbar, kbarc, kv.kbar_cur, kv.kbar_pool,
+        kv.kbar_win, kv.pool_count, kv.win_len, kv.win_id, sel, sel_count, srows, p.H, p.Nq, p.d,
+        p.T, p.W, p.C, QB, p.topk, scale, p.dev_status);
   else
-    chunk_means_kernel<float><<<g1, 256, 0, st>>>((const float *)q, (const float *)kv.k_cur, qbar,
-                                                  kv.kbar_cur, p.H, p.Nq, p.d, p.T, QB);
-  dim3 g2(QB, p.H, p.B);
-  score_topk_kernel<<<g2, 256, select_lds_bytes(p), st>>>(
-      qbar, kv.kbar_pool, kv.kbar_win, kv.kbar_cur, kv.pool_count, kv.win_len, kv.win_id, sel,
-      sel_count, srows, p.H, p.d, p.T, p.W, p.C, QB, p.topk, scale, p.dev_status);
-  if (masses) return launch_block_mass(p, mass_pool, mass_win, ws, st);
+    score_topk_kernel<float><<<g, 256, select_lds_bytes(p), st>>>(
+        (const float *)q, (const float *)kv.k_cur, qbar, kbarc, kv.kbar_cur, kv.kbar_pool,
+        kv.kbar_win, kv.pool_count, kv.win_len, kv.win_id, sel, sel_count, srows, p.H, p.Nq, p.d,
+        p.T, p.W, p.C, QB, p.topk, scale, p.dev_status);
+  if (masses) return launch_block_mass(p, scale, mass_pool, mass_win, ws, st);
   return hipGetLastError();
 }
 
@@ -428,15 +539,15 @@ hipError_t launch_select_static(const pbsa_problem &p, float scale, const void *
   return launch_select(p, scale, q, kv, sel, sel_count, mass_pool, mass_win, masses, ws, st);
 }
 
-hipError_t launch_block_mass(const pbsa_problem &p, float *mass_pool, float *mass_win,
-                             const void *ws, hipStream_t st) {
+hipError_t launch_block_mass(const pbsa_problem &p, float scale, float *mass_pool,
+                             float *mass_win, const void *ws, hipStream_t st) {
   const int QB = (p.Nq + p.T - 1) / p.T;
-  const size_t bh = (size_t)p.B * p.H;
-  const char *wsb = reinterpret_cast<const char *>(ws);
-  const float *srows = reinterpret_cast<const float *>(wsb + align256(bh * QB * p.d * sizeof(float)));
+  float *qbar, *srows, *kbarc;
+  select_ws_layout(p, ws, qbar, srows, kbarc);
   if (p.C + p.W > 0)
-    block_mass_kernel<<<dim3(p.H, p.B), kMassThreads, 0, st>>>(srows, mass_pool, mass_win, p.H, p.W,
-                                                                p.C, QB);
+    block_mass_kernel<<<dim3(p.H, p.B), kMassThreads, 0, st>>>(srows, qbar, kbarc, mass_pool,
+                                                                mass_win, p.H, p.W, p.C, QB, p.d,
+                                                                scale);
   return hipGetLastError();
 }
 
