@@ -9,8 +9,11 @@ window selection.  Per layer: pbsa_select -> pbsa_attn_fwd on the
 critical path, then pbsa_memory_update (the 37 blocks of chunk t-2 leave
 the window) -> pbsa_window_append (chunk t takes their slots) on a side
 stream: the next layer needs only the attention output, the updated cache is
-needed by the next chunk.  Inputs are synthetic
-(seeded, generated on the device) and resident in HBM before timing.
+needed by the next chunk.  Every timed step is the seeded Wan-chunk instance
+(layer l: seed 1000 + l, pool 0..31, window = chunks 2 and 3, 8 planted
+window blocks): the pool and window that the previous step's update and
+append changed are restored on the device before each step, outside the
+timing.  Inputs are synthetic, generated on the device and resident in HBM.
 
 Prints ONE JSON line: attention TFLOP/s over the whole step (algorithmic
 forward FLOPs 4*d*sum_rows|U_r| / step time), per-chunk latency, the forward
@@ -85,27 +88,49 @@ def build_rollout(n_layers, device):
 
 
 def time_steps(ro, steps, warmup, torch, sample_every=10):
-    """Whole-step timing + HIP events around a rotating sample of the forward
-    launches: in step s, the layers l with (l + s) % sample_every == 0, so
-    every layer is sampled over sample_every steps.  Each event pair delays
-    the launches after it by a few microseconds, so bracketing all 30
-    forwards would add ~2.5% to the step it measures.
-    Returns ms per step and [(layer, fwd ms)]."""
+    """Every step runs the seeded Wan-chunk instance itself: before it, each
+    layer's pool and window are restored to their seeded contents (device
+    copies on the critical-path stream, outside the timing), so the memory
+    update and window append of the previous step leave no trace.  The 30
+    layers' PBSA work runs between HIP events on that stream, and the steps
+    run back to back (no host synchronisation until the last one).  HIP
+    events also bracket a rotating sample of the forward launches: in step
+    s, the layers l with (l + s) % sample_every == 0, so every layer is
+    sampled over sample_every steps (each event pair delays the launches
+    after it by a few microseconds, so bracketing all 30 forwards would add
+    ~2.5% to the step it measures).
+    Returns ms per step (mean), [(step, layer, fwd ms)], per-layer FLOPs
+    (from the selections and pools the forwards saw) and the per-step ms."""
+    from block_sparse_attention_20_amd.rollout import attended_tokens
     n_layers = len(ro.layers)
+    d = ro.layers[0].d
+    seeded = ro.state_dict()
     for _ in range(warmup):
+        ro.load_state_dict(seeded)
         ro.run_chunk()
     torch.cuda.synchronize()
     ev = {(s, l): (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for s in range(steps) for l in range(n_layers) if (l + s) % sample_every == 0}
-    t0 = time.perf_counter()
+    step_ev, flops = [], [0] * n_layers
+    snaps = []
     for s in range(steps):
+        ro.load_state_dict(seeded)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         for l in range(n_layers):
             ro.run_layer(l, fwd_events=ev.get((s, l)))
+        e1.record()
+        if s == 0:  # routing of the seeded instance (the same every step)
+            snaps = [(L.t["sel"].clone(), L.t["sel_count"].clone()) for L in ro.layers]
+        step_ev.append((e0, e1))
         ro.advance()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    fwd_ms = [(l, a.elapsed_time(b)) for (s, l), (a, b) in sorted(ev.items())]
-    return (t1 - t0) * 1e3 / steps, fwd_ms
+    step_ms = [a.elapsed_time(b) for a, b in step_ev]
+    for l, L in enumerate(ro.layers):
+        flops[l] = 4 * d * attended_tokens(L, seeded["layers"][l]["pool_count"],
+                                           seeded["layers"][l]["pool_len"], *snaps[l])
+    fwd_ms = [(s, l, a.elapsed_time(b)) for (s, l), (a, b) in sorted(ev.items())]
+    return sum(step_ms) / steps, fwd_ms, flops, step_ms
 
 
 def breakdown(ro, torch, reps=3):
@@ -188,6 +213,10 @@ def rollout_bench(n_chunks, config_id, torch, n_layers=30, device="cuda"):
             ch = syn.make_chunk(shape, syn.rollout_seed(config_id, l, t), u, sigma=sigma, shift=1.5,
                                 n_planted=8, device=device)
             ro.set_inputs(l, ch["q"], ch["k"], ch["v"])
+        # the pools this chunk's forwards attend (each layer's update follows
+        # its forward), for the FLOP count after the chunk
+        ro.sync_side()
+        seen = [(L.t["pool_count"].clone(), L.t["pool_len"].clone()) for L in ro.layers]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for l in range(n_layers):
@@ -195,7 +224,7 @@ def rollout_bench(n_chunks, config_id, torch, n_layers=30, device="cuda"):
         e1.record()
         torch.cuda.synchronize()
         ms.append(e0.elapsed_time(e1))
-        gflop.append(sum(4 * s.d * attended_tokens(L) for L in ro.layers) / 1e9)
+        gflop.append(sum(4 * s.d * attended_tokens(L, *pl) for L, pl in zip(ro.layers, seen)) / 1e9)
         pool.append(int(ro.layers[0].t["pool_count"][0, 0].item()))
         ro.advance()
     steady = ms[4:]
@@ -621,20 +650,22 @@ def main():
     ro = build_rollout(args.layers, dev)
     torch.cuda.synchronize()
     log("timing")
-    ms, fwd_ms = time_steps(ro, args.steps, args.warmup, torch)
+    ms, fwd_samples, flops_layer, step_ms = time_steps(ro, args.steps, args.warmup, torch)
     d = ro.layers[0].d
-    flops_layer = [4 * d * attended_tokens(L) for L in ro.layers]
     step_flops = sum(flops_layer)
     value = step_flops / (ms * 1e-3) / 1e12
-    fwd_avg_ms = sum(x for _, x in fwd_ms) / len(fwd_ms)
-    fwd_tflops = sum(flops_layer[l] for l, _ in fwd_ms) / (sum(x for _, x in fwd_ms) * 1e-3) / 1e12
+    fwd_avg_ms = sum(x for _, _, x in fwd_samples) / len(fwd_samples)
+    # the sampled launches' own FLOPs: their layer's mean over the timed steps
+    fwd_tflops = (sum(flops_layer[l] for _, l, _ in fwd_samples)
+                  / (sum(x for _, _, x in fwd_samples) * 1e-3) / 1e12)
     bd = breakdown(ro, torch)
     out = {
         "metric": "PBSA attention TFLOP/s and per-chunk latency (ms) on one MI355X; % of MFMA peak",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "wan2.1-t2v-1.3b-shaped chunk, steady-state rollout step: "
+        "config": {"workload": "wan2.1-t2v-1.3b-shaped chunk, seeded instance (state restored "
+                               "before every step): "
                                f"{args.layers} layers x (select + fwd; update + append on a "
                                "side stream)",
                    "layers": args.layers, "heads": 12, "head_dim": d, "block": 128,
@@ -648,7 +679,9 @@ def main():
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": fwd_traffic_bytes(), "traffic_unit": "bytes per launch",
                      "launch_us": round(fwd_avg_ms * 1e3, 2),
-                     "launches": len(fwd_ms)},
+                     "launches": len(fwd_samples)},
+        "step_ms_min_median_max": [round(min(step_ms), 4), round(sorted(step_ms)[len(step_ms) // 2], 4),
+                                   round(max(step_ms), 4)],
         "breakdown_us_per_layer": bd,
     }
     if not args.no_train:

@@ -163,10 +163,17 @@ class Rollout:
         return attended_tokens(self.layers[layer])
 
 
-def attended_tokens(L: PBSALayer) -> int:
+def attended_tokens(L: PBSALayer, pool_count=None, pool_len=None, sel=None, sel_count=None) -> int:
     """Sum over (b, h, query row) of the valid key tokens each row attends:
-    pool slots [0, count) + selected window slots + the whole chunk."""
-    t = L.t
+    pool slots [0, count) + selected window slots + the whole chunk.
+    ``pool_count`` / ``pool_len`` / ``sel`` / ``sel_count``: the pool and
+    routing as a forward saw them, when the layer has moved on since
+    (default: the layer's current ones)."""
+    t = dict(L.t)
+    if pool_count is not None:
+        t["pool_count"], t["pool_len"] = pool_count, pool_len
+    if sel is not None:
+        t["sel"], t["sel_count"] = sel, sel_count
     T, Nq, QB = L.T, L.Nq, L.QB
     rows = torch.tensor([min(T, Nq - i * T) for i in range(QB)], dtype=torch.int64,
                         device=t["sel"].device)
