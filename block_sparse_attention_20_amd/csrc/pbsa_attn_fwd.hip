@@ -418,11 +418,15 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kerne
 
 // Merge of the split pieces, one workgroup per (query block, 32 of the d
 // output columns); thread t holds the same rows and columns as thread t of
-// the forward.  Two passes over the pieces in workgroup order: the max M of
-// their running maxima, then O = sum_g 2^(m_g - M) O_g / sum_g 2^(m_g - M) l_g.
-// The order is fixed, so the result does not depend on timing; the kernel
-// boundary orders the pieces' stores before these loads.  A split launch
-// cuts every query block into P >= 2 non-empty pieces, so each has a partial.
+// the forward.  The running max and row sum of every piece are loaded at
+// once (at most kMergePieces), then O = sum_g 2^(m_g - M) O_g / sum_g
+// 2^(m_g - M) l_g with M the max of the m_g, the partial O loads four pieces
+// at a time.  Sums run over the pieces in workgroup order, so the result
+// does not depend on timing; the kernel boundary orders the pieces' stores
+// before these loads.  A split launch cuts every query block into P >= 2
+// non-empty pieces, so each has a partial.
+constexpr int kMergePieces = 16;
+
 template <int D, int BT, typename TOut>
 __global__ __launch_bounds__(2 * BT) void attn_fwd_merge_kernel(FwdArgs a) {
   const int item = blockIdx.x / (D / 32), dt = blockIdx.x % (D / 32);
@@ -433,25 +437,44 @@ __global__ __launch_bounds__(2 * BT) void attn_fwd_merge_kernel(FwdArgs a) {
   const int l32 = lane & 31, g = lane >> 5;
   const int qrow = i * BT + wave * 32 + l32;
   auto slot_of = [&](int pc) -> size_t { return (size_t)pc * a.n_items + item; };
-  const int ga = 0, gb = a.P - 1;
+  float mg[kMergePieces], lg[kMergePieces];
+#pragma unroll
+  for (int gg = 0; gg < kMergePieces; ++gg) {
+    mg[gg] = -INFINITY;
+    lg[gg] = 0.f;
+    if (gg < a.P) {
+      const float *pm = a.part_ml + (slot_of(gg) * (2 * BT) + t) * 2;
+      mg[gg] = pm[0];
+      lg[gg] = pm[1];
+    }
+  }
   float M = -INFINITY;
-  for (int gg = ga; gg <= gb; ++gg) M = fmaxf(M, a.part_ml[(slot_of(gg) * (2 * BT) + t) * 2]);
+#pragma unroll
+  for (int gg = 0; gg < kMergePieces; ++gg) M = fmaxf(M, mg[gg]);
   float L = 0.f;
   float acc[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-#pragma unroll 2
-  for (int gg = ga; gg <= gb; ++gg) {
-    const size_t sl = slot_of(gg);
-    const float mg = a.part_ml[(sl * (2 * BT) + t) * 2], lg = a.part_ml[(sl * (2 * BT) + t) * 2 + 1];
-    const float w = mg == -INFINITY ? 0.f : exp2f(mg - M);
-    L += w * lg;
-    const float *po = a.part_o + ((sl * (D / 32) + dt) * (2 * BT) + t) * 16;
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(po + 4 * e4);
+  for (int g0 = 0; g0 < kMergePieces; g0 += 4) {
+    if (g0 >= a.P) break;
+    f32x4 v[4][4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc[4 * e4 + k] += w * v[k];
+    for (int u = 0; u < 4; ++u) {
+      const float *po = a.part_o + ((slot_of(g0 + u < a.P ? g0 + u : g0) * (D / 32) + dt) * (2 * BT) + t) * 16;
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) v[u][e4] = *reinterpret_cast<const f32x4 *>(po + 4 * e4);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (g0 + u < a.P) {
+        const float w = mg[g0 + u] == -INFINITY ? 0.f : exp2f(mg[g0 + u] - M);
+        L += w * lg[g0 + u];
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc[4 * e4 + k] += w * v[u][e4][k];
+      }
     }
   }
   if (qrow >= a.Nq) return;
@@ -736,6 +759,8 @@ constexpr int kMaxPieces = 8;
 // The fp32 path serves small problems, where a query block's list is a few
 // blocks: one piece per list entry, up to this many.
 constexpr int kMaxPiecesF32 = 16;
+static_assert(kMaxPieces <= kMergePieces && kMaxPiecesF32 <= kMergePieces,
+              "the merge loads every piece's running max and row sum at once");
 
 static int split_slots() {
   // per device, filled on first use; concurrent first calls store the same
