@@ -703,29 +703,50 @@ __global__ __launch_bounds__(256) void fwd_mass_reduce_kernel(FwdArgs a, float *
         } else {
           const int sc = max(0, min(a.sel_count[bh * a.QB + i], a.topk));
           const int32_t *sl = a.sel + (bh * a.QB + i) * (size_t)a.topk;
-          for (int e = 0; e < sc; ++e)
-            if (sl[e] == w) {
-              if (c == 0) f = n_pool + e;
-              ++c;
-            }
+          for (int e0 = 0; e0 < sc; e0 += 4) {
+            int32_t v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = e0 + u < sc ? sl[e0 + u] : -1;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (v[u] == w) {
+                if (c == 0) f = n_pool + e0 + u;
+                ++c;
+              }
+          }
         }
         first[t] = f;
         count[t] = c;
       }
       __syncthreads();
       const int ni = min(256, a.QB - i0);
-      for (int il = t / BT; il < ni; il += QPP) {
-        const int i = i0 + il, r = t % BT;
-        if (count[il] == 0 || i * BT + r >= a.Nq) continue;
-        const float L2 = a.lse[bh * a.Nq + (size_t)i * BT + r] * kLog2e;
-        const float *bl = a.blse + (((bh * a.QB + i) * (size_t)a.E) * BT) + r;
-        if (count[il] == 1) {
-          acc += exp2f(bl[(size_t)first[il] * BT] - L2);
-        } else {  // a slot listed more than once is attended once per listing
-          const int32_t *sl = a.sel + (bh * a.QB + i) * (size_t)a.topk;
-          const int sc = max(0, min(a.sel_count[bh * a.QB + i], a.topk));
-          for (int e = 0; e < sc; ++e)
-            if (sl[e] == w) acc += exp2f(bl[(size_t)(n_pool + e) * BT] - L2);
+      const int r = t % BT;
+      // four of this thread's (query block, row) pairs per round, their loads
+      // in flight together; terms added in ascending query block order
+      for (int il0 = t / BT; il0 < ni; il0 += 4 * QPP) {
+        float bv[4], lv[4];
+        int cnt[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int il = il0 + u * QPP, i = i0 + il;
+          cnt[u] = il < ni && i * BT + r < a.Nq ? count[il] : 0;
+          bv[u] = -INFINITY;
+          lv[u] = 0.f;
+          if (cnt[u] > 0) lv[u] = a.lse[bh * a.Nq + (size_t)i * BT + r];
+          if (cnt[u] == 1) bv[u] = a.blse[((bh * a.QB + i) * (size_t)a.E + first[il]) * BT + r];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (cnt[u] == 1) {
+            acc += exp2f(bv[u] - lv[u] * kLog2e);
+          } else if (cnt[u] > 1) {  // a slot listed more than once is attended once per listing
+            const int i = i0 + il0 + u * QPP;
+            const float *bl = a.blse + (((bh * a.QB + i) * (size_t)a.E) * BT) + r;
+            const int32_t *sl = a.sel + (bh * a.QB + i) * (size_t)a.topk;
+            const int sc = max(0, min(a.sel_count[bh * a.QB + i], a.topk));
+            for (int e = 0; e < sc; ++e)
+              if (sl[e] == w) acc += exp2f(bl[(size_t)(n_pool + e) * BT] - lv[u] * kLog2e);
+          }
         }
       }
       __syncthreads();
