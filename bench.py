@@ -5,21 +5,24 @@ Workload (one step = one chunk of a streaming rollout in steady state):
 the Wan2.1-T2V-1.3B-shaped chunk - 30 layers, each with 12 heads of 128, a
 4680-token chunk (37 blocks of 128, the last 72 tokens), a window of the two
 previous chunks (74 slots), a full persistent pool of 32 blocks and top-16
-window selection.  Per layer: pbsa_select -> pbsa_attn_fwd on the
-critical path, then pbsa_memory_update (the 37 blocks of chunk t-2 leave
-the window) -> pbsa_window_append (chunk t takes their slots) on a side
-stream: the next layer needs only the attention output, the updated cache is
-needed by the next chunk.  Every timed step is the seeded Wan-chunk instance
+window selection.  Per layer: pbsa_select_attn_fwd (each workgroup routes
+its query block, then attends: one launch) on the critical path, then
+pbsa_block_mass -> pbsa_memory_update (the 37 blocks of chunk t-2 leave the
+window) -> pbsa_window_append (chunk t takes their slots) on a side stream:
+the next layer needs only the attention output, the updated cache is needed
+by the next chunk.  Every timed step is the seeded Wan-chunk instance
 (layer l: seed 1000 + l, pool 0..31, window = chunks 2 and 3, 8 planted
 window blocks): the pool and window that the previous step's update and
 append changed are restored on the device before each step, outside the
 timing.  Inputs are synthetic, generated on the device and resident in HBM.
 
 Prints ONE JSON line: attention TFLOP/s over the whole step (algorithmic
-forward FLOPs 4*d*sum_rows|U_r| / step time), per-chunk latency, the forward
-kernel's roofline position (HIP events around a rotating sample of the
-forward launches inside the timed region, every layer sampled), a training step (batch 2, fwd + bwd) and the fp64 CPU
-oracle timed on a bounded sample of the same workload.
+forward FLOPs 4*d*sum_rows|U_r| / step time), per-chunk latency, the
+routing + forward kernel's roofline position (HIP events around a rotating
+sample of its launches inside the timed region, every layer sampled; the
+forward's FLOPs over the whole launch, routing included), a training step
+(batch 2, fwd + bwd) and the fp64 CPU oracle timed on a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -48,12 +51,12 @@ FWD_TRAFFIC = {"src_sha1": "86861af3fc5c657cfa3b957bd09563154aa2fb7c",
                "fetch_scale": 28302.0 / 14166.5, "write_scale": 28302.0 / 28304.3}
 
 
-FWD_SOURCES = ("pbsa_attn_fwd.hip", "pbsa_tiles.h")
+FWD_SOURCES = ("pbsa_attn_fwd.hip", "pbsa_tiles.h", "pbsa_select_dev.h")
 
 
 def fwd_source_sha1() -> str:
-    """sha1 over the forward kernel's sources (the kernel file and the tile
-    staging header it includes)."""
+    """sha1 over the forward kernel's sources (the kernel file and the
+    headers of tile staging and of the routing it runs first)."""
     import hashlib
     h = hashlib.sha1()
     for name in FWD_SOURCES:
@@ -137,12 +140,12 @@ def breakdown(ro, torch, reps=3):
     """Average device time of each call, run one after the other on one
     stream (separate, untimed pass)."""
     ro.sync_side()
-    names = ("select", "fwd", "update", "append")
+    names = ("select_fwd", "select", "fwd", "block_mass", "update", "append")
     acc = {n: [] for n in names}
     for _ in range(reps):
         t = ro.t
         for L in ro.layers:
-            calls = (L.select, L.fwd,
+            calls = (L.select_fwd, lambda: L.select(masses=False), L.fwd, L.block_mass,
                      lambda: L.update(ro.leaving[t % ro.window_chunks], ro.n_sink),
                      lambda: L.append_window(ro.first_slot(t), t * ro.QB))
             for n, fn in zip(names, calls):
@@ -673,15 +676,16 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "wan2.1-t2v-1.3b-shaped chunk, seeded instance (state restored "
                                "before every step): "
-                               f"{args.layers} layers x (select + fwd; update + append on a "
-                               "side stream)",
+                               f"{args.layers} layers x (select + fwd in one launch; block "
+                               "mass + update + append on a side stream)",
                    "layers": args.layers, "heads": 12, "head_dim": d, "block": 128,
                    "chunk_tokens": 4680, "window_slots": 74, "pool_blocks": 32, "topk": 16,
                    "parallelism": "1 GPU"},
         "per_chunk_latency_ms": round(ms, 4),
         "fwd_gflop_per_layer": round(step_flops / len(ro.layers) / 1e9, 2),
         "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"kernel": "attn_fwd_bf16_kernel<128,128>", "bound": "mfma",
+        "roofline": {"kernel": "attn_fwd_sel_bf16_kernel<128,128> (routing + forward)",
+                     "bound": "mfma",
                      "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": fwd_traffic_bytes(), "traffic_unit": "bytes per launch",

@@ -212,6 +212,27 @@ int pbsa_attn_fwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const
                                           ws_bytes, (hipStream_t)stream));
 }
 
+int pbsa_select_attn_fwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, int32_t *sel,
+                         int32_t *sel_count, void *o, float *lse, void *ws, size_t ws_bytes,
+                         void *fwd_ws, size_t fwd_ws_bytes, pbsa_stream_t stream) {
+  int rc = check_problem(p, PBSA_OP_SELECT);
+  if (rc) return rc;
+  REQ(q);
+  if ((rc = check_kv_common(kv, p))) return rc;
+  REQ(kv->kbar_cur);
+  if (p->W > 0) REQ(kv->kbar_win);
+  if (p->C > 0) REQ(kv->kbar_pool);
+  if (p->topk > 0) REQ(sel);
+  REQ(sel_count);
+  REQ(o);
+  if (lse && !aligned16(lse)) return fail(PBSA_ERR_ALIGN, "lse is not 16-byte aligned");
+  if ((rc = check_ws(p, PBSA_OP_SELECT, ws, ws_bytes))) return rc;
+  if (fwd_ws != nullptr && !aligned16(fwd_ws))
+    return fail(PBSA_ERR_ALIGN, "fwd_ws is not 16-byte aligned");
+  return hip_status(pbsa::launch_select_attn_fwd(*p, eff_scale(p), q, *kv, sel, sel_count, o, lse,
+                                                 ws, fwd_ws, fwd_ws_bytes, (hipStream_t)stream));
+}
+
 int pbsa_attn_bwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const int32_t *sel,
                   const int32_t *sel_count, const void *o, const float *lse, const void *dout,
                   void *dq, const pbsa_kv_grad *g, void *ws, size_t ws_bytes,

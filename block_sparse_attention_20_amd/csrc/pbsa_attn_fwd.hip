@@ -40,6 +40,7 @@
 // same split and merge (small problems).
 #include "pbsa_common.h"
 #include "pbsa_internal.h"
+#include "pbsa_select_dev.h"
 #include "pbsa_tiles.h"
 
 #include <atomic>
@@ -113,10 +114,13 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// sel_lds: the query block's selection already in LDS (n_sel entries; the
+// fused select + forward), else nullptr (read from a.sel / a.sel_count).
 template <int D, int BT, bool MASS>
 __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh, uint16_t *K0,
                                             uint16_t *K1, uint16_t *V0, uint16_t *V1, int wg, int item,
-                                            int j0, int j1) {
+                                            int j0, int j1, const int32_t *sel_lds = nullptr,
+                                            int n_sel = 0) {
   constexpr int NW = BT / 32;  // waves; wave w owns query rows [32w, 32w+32)
   constexpr int TT = kTile;
   using G = DmaGeom<D, TT, NW>;
@@ -132,8 +136,15 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  int n_pool, sc;
-  const int nb = clamp_counts(a, bh, i, n_pool, sc);
+  int n_pool, sc, nb;
+  if (sel_lds) {
+    n_pool = a.pool_count[bh];
+    n_pool = max(0, min(n_pool, a.C));  // the routing has flagged a bad count
+    sc = n_sel;
+    nb = n_pool + sc + a.QB;
+  } else {
+    nb = clamp_counts(a, bh, i, n_pool, sc);
+  }
   const int jend = min(j1, nb);
 
   // this lane's query column, held as MFMA B fragments for the whole kernel
@@ -184,7 +195,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
   dma_lane_offsets<D, TT, NW, kSwzK>(lane, kdma);
   dma_lane_offsets<D, TT, NW, kSwzV>(lane, vdma);
   __syncthreads();  // the previous segment of this workgroup is done with LDS
-  preload_list<D, BT>(a, bh, i, n_pool, sc, blist, t, 2 * BT);
+  preload_list<D, BT>(a, bh, i, n_pool, sc, blist, t, 2 * BT, sel_lds);
   __syncthreads();
 
   // tile stream: (block j, half h); tile rows = min(64, len_j - 64 h)
@@ -414,6 +425,36 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kerne
   const int pc = wg / a.n_items;
   fwd_segment<D, BT, MASS>(a, sh, K0, K1, V0, V1, wg, wg % a.n_items, piece_start(a, pc),
                            piece_start(a, pc + 1));
+}
+
+// Select + forward in one launch (d = T = 128, bf16, no split): each
+// workgroup first routes its own query block (select_query_block: the same
+// code and order as the select kernel, so sel, sel_count, the means and the
+// score rows are bit-identical), then attends with the selection it holds
+// in LDS.  The routing's scratch borrows the second K and V tile buffers,
+// which the walk first fills during the first tile (after the routing is
+// done); it needs 16 KB of each: 2 x 256 x 8 floats of partial sums, and
+// 20 B per window slot (W <= 819).  The block list takes at most 128
+// entries (C + topk <= 128), all resolved from LDS.
+constexpr int kFusedMaxW = (kTile * 128 * 2) / 20;
+
+template <int D, int BT>
+__global__ __launch_bounds__(2 * BT, 2) void attn_fwd_sel_bf16_kernel(FwdArgs a,
+                                                                      SelArgs<uint16_t> s) {
+  static_assert(D == 128 && BT == 128, "the routing runs on 256 threads with 16 KB tile buffers");
+  __shared__ FwdLds<D, BT> sh;
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[kTile * D], K1[kTile * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[kTile * D], V1[kTile * D];
+  __shared__ __attribute__((aligned(16))) float qv[128];
+  __shared__ float both[256];
+  __shared__ int nvalid, wcnt[4], n_sel;
+  __shared__ int32_t sel_lds[kMaxList];
+  int wg;
+  item_of_block(a, wg);
+  if (wg >= a.n_items) return;
+  const SelLds L{qv, reinterpret_cast<float *>(K1), both, V1, &nvalid, wcnt, sel_lds, &n_sel};
+  select_query_block<uint16_t>(s, wg % a.QB, (size_t)(wg / a.QB), L);
+  fwd_segment<D, BT, false>(a, sh, K0, K1, V0, V1, wg, wg, 0, a.NB, sel_lds, n_sel);
 }
 
 // Merge of the split pieces, one workgroup per (query block, 32 of the d
@@ -843,13 +884,10 @@ hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, co
                               nullptr, nullptr, st);
 }
 
-// blse == nullptr: plain forward; else the MASS kernels and the reduce into
-// mass_pool / mass_win (lse required)
-static hipError_t launch_attn_fwd_impl(const pbsa_problem &p, float scale, const void *q,
-                                       const pbsa_kv &kv, const int32_t *sel,
-                                       const int32_t *sel_count, void *o, float *lse, void *ws,
-                                       size_t ws_bytes, float *blse, float *mass_pool,
-                                       float *mass_win, hipStream_t st) {
+// The forward's arguments, unsplit.
+static FwdArgs fwd_args(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
+                        const int32_t *sel, const int32_t *sel_count, void *o, float *lse,
+                        float *blse) {
   FwdArgs a;
   a.q = q;
   a.k_cur = kv.k_cur; a.v_cur = kv.v_cur; a.k_win = kv.k_win; a.v_win = kv.v_win;
@@ -867,16 +905,52 @@ static hipError_t launch_attn_fwd_impl(const pbsa_problem &p, float scale, const
   a.part_o = a.part_ml = nullptr;
   a.blse = blse;
   a.E = p.C + p.topk > 0 ? p.C + p.topk : 1;
-  int n_wg = a.n_items;
-  const int64_t slots = split_slots();
-  // The split pays off only when one workgroup per query block would leave
-  // most resident slots idle; otherwise the partials and their merge only
-  // add traffic.  It needs at least two pieces of at least one list entry
-  // each (a one-entry list is never split).
-  int64_t pcs = slots / a.n_items;
+  a.per_xcd = (a.n_items + 7) / 8;
+  return a;
+}
+
+// Pieces per query block a split launch would cut (given a workspace): the
+// split pays off only when one workgroup per query block would leave most
+// resident slots idle; otherwise the partials and their merge only add
+// traffic.  It needs at least two pieces of at least one list entry each
+// (a one-entry list is never split).
+static int64_t split_pieces(const pbsa_problem &p, const FwdArgs &a) {
+  int64_t pcs = split_slots() / a.n_items;
   const int max_pieces = p.dtype == PBSA_BF16 ? kMaxPieces : kMaxPiecesF32;
   if (pcs > max_pieces) pcs = max_pieces;
   if (pcs > a.NB) pcs = a.NB;
+  return pcs;
+}
+
+hipError_t launch_select_attn_fwd(const pbsa_problem &p, float scale, const void *q,
+                                  const pbsa_kv &kv, int32_t *sel, int32_t *sel_count, void *o,
+                                  float *lse, void *ws, void *fwd_ws, size_t fwd_bytes,
+                                  hipStream_t st) {
+  FwdArgs a = fwd_args(p, scale, q, kv, sel, sel_count, o, lse, nullptr);
+  const bool would_split = fwd_ws != nullptr && fwd_bytes >= fwd_ws_bytes(p) &&
+                           split_pieces(p, a) >= 2;
+  const bool fused = p.dtype == PBSA_BF16 && p.d == 128 && p.T == 128 &&
+                     p.C + p.topk <= kMaxList && p.W <= kFusedMaxW && !would_split;
+  if (!fused) {
+    hipError_t e = launch_select(p, scale, q, kv, sel, sel_count, nullptr, nullptr, false, ws, st);
+    if (e != hipSuccess) return e;
+    return launch_attn_fwd(p, scale, q, kv, sel, sel_count, o, lse, fwd_ws, fwd_bytes, st);
+  }
+  attn_fwd_sel_bf16_kernel<128, 128><<<dim3(8 * a.per_xcd), dim3(256), 0, st>>>(
+      a, sel_args<uint16_t>(p, scale, q, kv, sel, sel_count, ws));
+  return hipGetLastError();
+}
+
+// blse == nullptr: plain forward; else the MASS kernels and the reduce into
+// mass_pool / mass_win (lse required)
+static hipError_t launch_attn_fwd_impl(const pbsa_problem &p, float scale, const void *q,
+                                       const pbsa_kv &kv, const int32_t *sel,
+                                       const int32_t *sel_count, void *o, float *lse, void *ws,
+                                       size_t ws_bytes, float *blse, float *mass_pool,
+                                       float *mass_win, hipStream_t st) {
+  FwdArgs a = fwd_args(p, scale, q, kv, sel, sel_count, o, lse, blse);
+  int n_wg = a.n_items;
+  const int64_t pcs = split_pieces(p, a);
   if (ws != nullptr && ws_bytes >= fwd_ws_bytes(p) && pcs >= 2) {
     a.split = 1;
     a.P = (int)pcs;

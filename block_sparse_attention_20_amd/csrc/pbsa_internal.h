@@ -16,6 +16,9 @@ size_t select_ws_bytes(const pbsa_problem &p);
 // Wan chunk needs 0.5 MB, batch 8 of it 3.9 MB)
 constexpr size_t kSelectScratchBytes = size_t(8) << 20;
 size_t select_lds_bytes(const pbsa_problem &p);
+// select workspace: query-block means, score rows, current-block key means
+void select_ws_layout(const pbsa_problem &p, const void *ws, float *&qbar, float *&srows,
+                      float *&kbarc);
 size_t update_ws_bytes(const pbsa_problem &p);
 size_t fwd_ws_bytes(const pbsa_problem &p);
 size_t fwd_mass_ws_bytes(const pbsa_problem &p);
@@ -38,6 +41,13 @@ hipError_t launch_window_append(const pbsa_problem &p, const pbsa_kv &kv, void *
 hipError_t launch_attn_fwd(const pbsa_problem &p, float scale, const void *q, const pbsa_kv &kv,
                            const int32_t *sel, const int32_t *sel_count, void *o, float *lse,
                            void *ws, size_t ws_bytes, hipStream_t st);
+// select (no masses) + forward in one launch where the problem allows it
+// (bf16, d = T = 128, C + topk <= 128, W <= 819, no split), else the two
+// launches; ws = the select workspace, fwd_ws the forward's (optional)
+hipError_t launch_select_attn_fwd(const pbsa_problem &p, float scale, const void *q,
+                                  const pbsa_kv &kv, int32_t *sel, int32_t *sel_count, void *o,
+                                  float *lse, void *ws, void *fwd_ws, size_t fwd_ws_bytes,
+                                  hipStream_t st);
 hipError_t launch_attn_fwd_mass(const pbsa_problem &p, float scale, const void *q,
                                 const pbsa_kv &kv, const int32_t *sel, const int32_t *sel_count,
                                 void *o, float *lse, float *mass_pool, float *mass_win, void *ws,

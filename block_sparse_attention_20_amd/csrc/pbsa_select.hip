@@ -20,6 +20,7 @@
 // block masses, and are formed by the block-mass kernel, which runs later.
 #include "pbsa_common.h"
 #include "pbsa_internal.h"
+#include "pbsa_select_dev.h"
 
 #include <mutex>
 
@@ -66,57 +67,6 @@ __device__ void block_mean_wg(const TIn *__restrict__ src, int n, int d, float *
   __syncthreads();
 }
 
-// Means of the first n rows of two [rows, d] blocks a and b (row stride d)
-// at once, so that both blocks' loads are in flight together; fp32 sums in
-// a fixed order.  256 threads, 16-byte loads; red: LDS, >= 2*256*8 floats.
-// Threads [0, d) write out_a[t], threads [d, 2d) out_b[t - d]; both means
-// also go to both[0, 2d) (LDS).
-template <typename TIn>
-__device__ void two_block_means(const TIn *__restrict__ a, const TIn *__restrict__ b, int n, int d,
-                                float *out_a, float *out_b, float *red, float *both) {
-  constexpr int E = 16 / sizeof(TIn);
-  const int tpr = d / E, rpp = 256 / tpr;
-  const int t = threadIdx.x;
-  const int rg = t / tpr, cg = t % tpr;
-  float acc[2][E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[0][e] = acc[1][e] = 0.f;
-#pragma unroll 8
-  for (int r = rg; r < n; r += rpp) {
-    const u32x4 va = *reinterpret_cast<const u32x4 *>(a + (size_t)r * d + cg * E);
-    const u32x4 vb = *reinterpret_cast<const u32x4 *>(b + (size_t)r * d + cg * E);
-    if constexpr (sizeof(TIn) == 2) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[0][2 * e] += bflo(va[e]);
-        acc[0][2 * e + 1] += bfhi(va[e]);
-        acc[1][2 * e] += bflo(vb[e]);
-        acc[1][2 * e + 1] += bfhi(vb[e]);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[0][e] += __uint_as_float(va[e]);
-        acc[1][e] += __uint_as_float(vb[e]);
-      }
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    red[rg * d + cg * E + e] = acc[0][e];
-    red[256 * 8 + rg * d + cg * E + e] = acc[1][e];
-  }
-  __syncthreads();
-  if (t < 2 * d) {
-    const int c = t % d, w = t / d;
-    float s = 0.f;
-    for (int g = 0; g < rpp; ++g) s += red[w * 256 * 8 + g * d + c];
-    const float v = n > 0 ? s / (float)n : 0.f;
-    if (w == 0) out_a[c] = v; else out_b[c] = v;
-    both[t] = v;  // [a | b], for the caller (after a sync)
-  }
-}
-
 // grid (n_blocks): means of stored slot blocks [n, T, d] with lengths
 template <typename TIn>
 __global__ __launch_bounds__(256) void slot_means_kernel(const TIn *__restrict__ x,
@@ -134,177 +84,20 @@ __global__ __launch_bounds__(256) void slot_means_kernel(const TIn *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Own-block means, coarse scores + window top-k.  grid (QB, H, B), 256 threads.
-//  - the query block's Q rows and K rows (the current chunk's block i) are
-//    averaged together: qbar_i to LDS and to the workspace (for the block
-//    mass), kbar_cur_i to its cache;
-//  - candidates [pool C | window W], 16 lanes per candidate (coalesced
-//    16-byte reads of kbar, 4 shuffles); the first batch of candidate loads
-//    is issued before the means are reduced;
-//  - the score row's pool and window part goes to the workspace for the
-//    block-mass kernel (which adds the current-chunk part);
-//  - top-k is rank based: a valid window slot is selected iff fewer than k
-//    valid slots rank before it in the total order (score desc, id asc, NaN
-//    last); its output position is the number of selected slots below it.
-//    Exact and order-independent, hence deterministic.  Scores enter the
-//    ranking as order keys (order_key; 0 = invalid slot), so the pairwise
-//    comparisons are branch free.
+// Own-block means, coarse scores + window top-k (select_query_block, shared
+// with the fused select + forward kernel).  grid (QB, H, B), 256 threads.
 // Dynamic LDS: window ids [W] int64, keys [W], flags [W], ranks [W].
 // ---------------------------------------------------------------------------
-// 16 candidates per pass; 7 passes cover the 106 pool and window candidates
-// of the Wan chunk (pool 32 + window 74) with one batch of loads.
-constexpr int kScorePasses = 7;
-
 template <typename TIn>
-__global__ __launch_bounds__(256) void score_topk_kernel(
-    const TIn *__restrict__ q, const TIn *__restrict__ k_cur, float *__restrict__ qbar_out,
-    float *__restrict__ kbarc_out, float *__restrict__ kbar_cur, const float *__restrict__ kbar_pool,
-    const float *__restrict__ kbar_win, const int32_t *__restrict__ pool_count,
-    const int32_t *__restrict__ win_len, const int64_t *__restrict__ win_id,
-    int32_t *__restrict__ sel, int32_t *__restrict__ sel_count, float *__restrict__ srow_out,
-    int H, int Nq, int d, int T, int W, int C, int QB, int topk, float scale, int32_t *status) {
+__global__ __launch_bounds__(256) void score_topk_kernel(SelArgs<TIn> s) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ __attribute__((aligned(16))) float qv[128];
   __shared__ float red[2 * 256 * 8];
   __shared__ float both[256];
-  int64_t *wid = reinterpret_cast<int64_t *>(smem);          // [W]
-  uint32_t *key = reinterpret_cast<uint32_t *>(wid + W);  // [W]: order keys
-  int *flag = reinterpret_cast<int *>(key + W);           // [W]: 1 valid, 2 selected
-  int *rank = flag + W;                                    // [W]
   __shared__ int nvalid_sh;
   __shared__ int wcnt[4];
-
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const size_t bh = (size_t)b * H + h;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  int n_pool = pool_count[bh];
-  if (n_pool < 0 || n_pool > C) {
-    if (t == 0) set_status(status, PBSA_STATUS_POOL_COUNT);
-    n_pool = max(0, min(n_pool, C));
-  }
-  int nv = 0;
-  for (int w = t; w < W; w += 256) {
-    const int len = win_len[w];
-    if (len > T) set_status(status, PBSA_STATUS_WIN_LEN);
-    flag[w] = len > 0 ? 1 : 0;
-    nv += len > 0;
-    wid[w] = win_id[w];
-  }
-  if (t == 0) nvalid_sh = 0;
-  const int nj = C + W;                 // candidates scored here
-  const int nrow = C + W + QB;          // score row length (current part: block mass)
-  const int sub = lane >> 4, sl = lane & 15;
-  const int per = d / 16;  // floats per lane (8 or 4)
-  float *srow = srow_out + (bh * QB + i) * (size_t)nrow;
-  // one batch of candidate loads (the first kScorePasses * 16 candidates)
-  auto load_batch = [&](int base, f32x4 (&k0)[kScorePasses], f32x4 (&k1)[kScorePasses],
-                        bool (&ok)[kScorePasses]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int ps = 0; ps < kScorePasses; ++ps) {
-      const int j = base + ps * 16 + sub;
-      const float *kb = kbar_pool;
-      bool valid = false;
-      if (j < C) {
-        valid = j < n_pool;
-        kb = kbar_pool + (bh * C + j) * d;
-      } else if (j < nj) {
-        valid = win_len[j - C] > 0;
-        kb = kbar_win + (bh * W + (j - C)) * d;
-      }
-      ok[ps] = valid;
-      k0[ps] = f32x4{0.f, 0.f, 0.f, 0.f};
-      k1[ps] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (valid) {
-        k0[ps] = *reinterpret_cast<const f32x4 *>(kb + sl * per);
-        if (per == 8) k1[ps] = *reinterpret_cast<const f32x4 *>(kb + sl * per + 4);
-      }
-    }
-  };
-  f32x4 k0[kScorePasses], k1[kScorePasses];
-  bool ok[kScorePasses];
-  int base = wave * 4;
-  load_batch(base, k0, k1, ok);
-  // the block's own means (Q -> qbar, K -> kbar_cur)
-  {
-    const int r0 = i * T, n = min(T, Nq - r0);
-    two_block_means<TIn>(q + (bh * Nq + r0) * d, k_cur + (bh * Nq + r0) * d, n, d, qv,
-                         kbar_cur + (bh * QB + i) * d, red, both);
-  }
-  __syncthreads();
-  if (t < d) {
-    qbar_out[(bh * QB + i) * d + t] = qv[t];
-    kbarc_out[(bh * QB + i) * d + t] = both[d + t];
-  }
-  for (int o = 32; o > 0; o >>= 1) nv += __shfl_xor(nv, o);
-  if (lane == 0) atomicAdd(&nvalid_sh, nv);
-  for (;;) {
-#pragma unroll
-    for (int ps = 0; ps < kScorePasses; ++ps) {
-      const int j = base + ps * 16 + sub;
-      const float *qq = qv + sl * per;
-      float acc = qq[0] * k0[ps][0] + qq[1] * k0[ps][1] + qq[2] * k0[ps][2] + qq[3] * k0[ps][3];
-      if (per == 8) acc += qq[4] * k1[ps][0] + qq[5] * k1[ps][1] + qq[6] * k1[ps][2] + qq[7] * k1[ps][3];
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      acc += __shfl_xor(acc, 4);
-      acc += __shfl_xor(acc, 8);
-      if (sl == 0 && j < nj) {
-        const float v = ok[ps] ? acc * scale : -INFINITY;
-        srow[j] = v;
-        if (j >= C) key[j - C] = ok[ps] ? order_key(v) : 0u;
-      }
-    }
-    base += 16 * kScorePasses;
-    if (base >= nj) break;
-    load_batch(base, k0, k1, ok);
-  }
-  __syncthreads();
-
-  // rank-based top-k over the valid window slots: a slot is selected iff
-  // fewer than k valid slots rank before it.  The comparisons are split
-  // over the four waves (each takes a quarter of the v range for every w);
-  // partial ranks meet in LDS.
-  for (int w = t; w < W; w += 256) rank[w] = 0;
-  __syncthreads();
-  {
-    const int vq = (W + 3) / 4, v0 = wave * vq, v1 = min(W, v0 + vq);
-    for (int w = lane; w < W; w += 64) {
-      const uint32_t kw = key[w];
-      const int64_t iw = wid[w];
-      int r = 0;
-      // an invalid v has key 0 and never ranks before a valid w; v == w
-      // fails both terms
-#pragma unroll 8
-      for (int v = v0; v < v1; ++v) {
-        const uint32_t kv = key[v];
-        r += (int)((kv > kw) | ((kv == kw) & (wid[v] < iw)));
-      }
-      if (r && kw != 0) atomicAdd(&rank[w], r);
-    }
-  }
-  __syncthreads();
-  for (int w = t; w < W; w += 256)
-    if ((flag[w] & 1) && rank[w] < topk) flag[w] |= 2;
-  __syncthreads();
-  const int n_sel = min(topk, nvalid_sh);
-  int32_t *selrow = sel + (bh * QB + i) * (size_t)topk;
-  // positions: ascending slot order, by ballot prefix counts per 256 slots
-  int carry = 0;
-  for (int base = 0; base < W; base += 256) {
-    const int w = base + t;
-    const bool bit = w < W && (flag[w] & 2);
-    const unsigned long long m = __ballot(bit);
-    if (lane == 0) wcnt[wave] = __popcll(m);
-    __syncthreads();
-    int before = carry;
-    for (int q = 0; q < wave; ++q) before += wcnt[q];
-    const int pos = before + __popcll(m & ((1ull << lane) - 1ull));
-    if (bit && pos < topk) selrow[pos] = w;  // more than k only with duplicate ids
-    carry += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
-    __syncthreads();
-  }
-  for (int p = n_sel + t; p < topk; p += 256) selrow[p] = -1;
-  if (t == 0) sel_count[bh * QB + i] = n_sel;
+  const SelLds L{qv, red, both, smem, &nvalid_sh, wcnt, nullptr, nullptr};
+  select_query_block<TIn>(s, blockIdx.x, (size_t)blockIdx.z * s.H + blockIdx.y, L);
 }
 
 // ---------------------------------------------------------------------------
@@ -459,8 +252,8 @@ size_t select_ws_bytes(const pbsa_problem &p) {
          align256(bh * QB * (p.C + p.W + QB) * sizeof(float));
 }
 
-static void select_ws_layout(const pbsa_problem &p, const void *ws, float *&qbar, float *&srows,
-                             float *&kbarc) {
+void select_ws_layout(const pbsa_problem &p, const void *ws, float *&qbar, float *&srows,
+                      float *&kbarc) {
   const size_t QB = (p.Nq + p.T - 1) / p.T;
   const size_t bh = (size_t)p.B * p.H;
   char *w = reinterpret_cast<char *>(const_cast<void *>(ws));
@@ -479,19 +272,13 @@ hipError_t launch_select(const pbsa_problem &p, float scale, const void *q, cons
                          int32_t *sel, int32_t *sel_count, float *mass_pool, float *mass_win,
                          bool masses, void *ws, hipStream_t st) {
   const int QB = (p.Nq + p.T - 1) / p.T;
-  float *qbar, *srows, *kbarc;
-  select_ws_layout(p, ws, qbar, srows, kbarc);
   const dim3 g(QB, p.H, p.B);
   if (p.dtype == PBSA_BF16)
     score_topk_kernel<uint16_t><<<g, 256, select_lds_bytes(p), st>>>(
-        (const uint16_t *)q, (const uint16_t *)kv.k_cur, qbar, kbarc, kv.kbar_cur, kv.kbar_pool,
-        kv.kbar_win, kv.pool_count, kv.win_len, kv.win_id, sel, sel_count, srows, p.H, p.Nq, p.d,
-        p.T, p.W, p.C, QB, p.topk, scale, p.dev_status);
+        sel_args<uint16_t>(p, scale, q, kv, sel, sel_count, ws));
   else
     score_topk_kernel<float><<<g, 256, select_lds_bytes(p), st>>>(
-        (const float *)q, (const float *)kv.k_cur, qbar, kbarc, kv.kbar_cur, kv.kbar_pool,
-        kv.kbar_win, kv.pool_count, kv.win_len, kv.win_id, sel, sel_count, srows, p.H, p.Nq, p.d,
-        p.T, p.W, p.C, QB, p.topk, scale, p.dev_status);
+        sel_args<float>(p, scale, q, kv, sel, sel_count, ws));
   if (masses) return launch_block_mass(p, scale, mass_pool, mass_win, ws, st);
   return hipGetLastError();
 }

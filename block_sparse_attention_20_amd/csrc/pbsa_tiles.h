@@ -194,9 +194,12 @@ struct BlockList {
   int32_t meta[kMaxList];
 };
 
+// selrow: the query block's selected window slots; nullptr = its row of
+// a.sel.
 template <int D, int BT, typename Args>
 __device__ __forceinline__ void preload_list(const Args &a, size_t bh, int i, int n_pool, int sc,
-                                             BlockList &bl, int t, int nt) {
+                                             BlockList &bl, int t, int nt,
+                                             const int32_t *selrow = nullptr) {
   const int n = min(n_pool + sc, kMaxList);
   for (int j = t; j < n; j += nt) {
     int64_t off;
@@ -205,7 +208,7 @@ __device__ __forceinline__ void preload_list(const Args &a, size_t bh, int i, in
       off = (int64_t)(bh * a.C + j) * (BT * D);
       len = a.pool_len[bh * a.C + j];
     } else {
-      const int w = a.sel[(bh * a.QB + i) * (size_t)a.topk + (j - n_pool)];
+      const int w = selrow ? selrow[j - n_pool] : a.sel[(bh * a.QB + i) * (size_t)a.topk + (j - n_pool)];
       win = 1;
       if (w < 0 || w >= a.W) {
         set_status(a.status, PBSA_STATUS_SEL);

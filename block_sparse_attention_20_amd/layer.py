@@ -96,6 +96,14 @@ class PBSALayer:
                       t["sel_count"], t["mass_pool"] if masses and self.C > 0 else None,
                       t["mass_win"] if masses and self.W > 0 else None, self.ws_select)
 
+    def select_fwd(self, with_lse=True):
+        """select(masses=False) then fwd() as one call (pbsa_select_attn_fwd):
+        one launch where the problem allows, the same results bit for bit."""
+        t = self.t
+        P.pbsa_select_attn_fwd(self.prob, t["q"], self.kv, t["sel"] if self.topk > 0 else None,
+                               t["sel_count"], t["o"], t["lse"] if with_lse else None,
+                               self.ws_select, self.ws_fwd)
+
     def block_mass(self):
         t = self.t
         P.pbsa_block_mass(self.prob, t["mass_pool"] if self.C > 0 else None,

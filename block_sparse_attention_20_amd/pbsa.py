@@ -20,11 +20,13 @@ PBSA_BF16, PBSA_F32 = 0, 1
 PBSA_OP_SELECT, PBSA_OP_FWD, PBSA_OP_BWD, PBSA_OP_UPDATE, PBSA_OP_FINE_MASS = 0, 1, 2, 3, 4
 PBSA_OP_FWD_MASS = 5
 PBSA_STATUS_POOL_COUNT, PBSA_STATUS_WIN_LEN, PBSA_STATUS_SEL, PBSA_STATUS_SINK = 1, 2, 4, 8
+(PBSA_OK, PBSA_ERR_NULL, PBSA_ERR_SHAPE, PBSA_ERR_DTYPE, PBSA_ERR_ALIGN, PBSA_ERR_WORKSPACE,
+ PBSA_ERR_HIP, PBSA_ERR_UNSUPPORTED) = 0, -1, -2, -3, -4, -5, -6, -7
 PBSA_STATUS_SHARED = 16
 
 # every exported symbol declared in include/pbsa.h
 EXPORTS = ("pbsa_select", "pbsa_select_static", "pbsa_block_mass", "pbsa_attn_fwd",
-           "pbsa_attn_fwd_mass", "pbsa_attn_bwd", "pbsa_memory_update",
+           "pbsa_attn_fwd_mass", "pbsa_select_attn_fwd", "pbsa_attn_bwd", "pbsa_memory_update",
            "pbsa_fine_mass", "pbsa_memory_update_shared", "pbsa_block_gather", "pbsa_grad_scatter",
            "pbsa_block_mean", "pbsa_window_append", "pbsa_workspace_size", "pbsa_validate",
            "pbsa_strerror", "pbsa_last_error")
@@ -77,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "pbsa_block_mass": (ctypes.c_int, [P, vp, vp, vp, sz, vp]),
             "pbsa_attn_fwd": (ctypes.c_int, [P, vp, K, vp, vp, vp, vp, vp, sz, vp]),
             "pbsa_attn_fwd_mass": (ctypes.c_int, [P, vp, K, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "pbsa_select_attn_fwd": (ctypes.c_int, [P, vp, K, vp, vp, vp, vp, vp, sz, vp, sz, vp]),
             "pbsa_attn_bwd": (ctypes.c_int, [P, vp, K, vp, vp, vp, vp, vp, vp, G, vp, sz, vp]),
             "pbsa_memory_update": (ctypes.c_int, [P, K, vp, vp, vp, i32, i64, vp, sz, vp]),
             "pbsa_fine_mass": (ctypes.c_int, [P, vp, K, vp, vp, vp, vp, vp, vp, sz, vp]),
@@ -155,6 +158,15 @@ def pbsa_attn_fwd(prob, q, kv: KV, sel, sel_count, o, lse, ws=None, stream=None)
                                _p(o), _p(lse), _p(ws),
                                0 if ws is None else ws.numel() * ws.element_size(),
                                _stream(stream)))
+
+
+def pbsa_select_attn_fwd(prob, q, kv: KV, sel, sel_count, o, lse, ws, fwd_ws=None, stream=None):
+    _check(lib().pbsa_select_attn_fwd(ctypes.byref(prob), _p(q), ctypes.byref(kv), _p(sel),
+                                      _p(sel_count), _p(o), _p(lse), _p(ws),
+                                      0 if ws is None else ws.numel() * ws.element_size(),
+                                      _p(fwd_ws),
+                                      0 if fwd_ws is None else fwd_ws.numel() * fwd_ws.element_size(),
+                                      _stream(stream)))
 
 
 def pbsa_attn_fwd_mass(prob, q, kv: KV, sel, sel_count, o, lse, mass_pool, mass_win, ws,

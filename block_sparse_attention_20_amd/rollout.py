@@ -50,10 +50,13 @@ class Rollout:
     def __init__(self, n_layers: int, B: int, H: int, d: int, T: int, Nq: int, C: int, topk: int,
                  n_sink: int = 0, window_chunks: int = 2, dtype=torch.bfloat16, scale: float = 0.0,
                  device="cuda", overlap: bool = False, mass: str = "coarse",
-                 shared_pool: bool = False):
+                 shared_pool: bool = False, fused: bool = True):
         if mass not in ("coarse", "fine"):
             raise ValueError(f"mass must be 'coarse' or 'fine', not {mass!r}")
         self.mass = mass
+        # select + forward through pbsa_select_attn_fwd (one launch where the
+        # problem allows) instead of pbsa_select then pbsa_attn_fwd
+        self.fused = fused
         self.shared_pool = shared_pool
         self.QB = (Nq + T - 1) // T
         self.window_chunks = window_chunks
@@ -99,19 +102,26 @@ class Rollout:
         L = self.layers[layer]
         t = self.t
         self._wait_side(layer)
+        fine_now = self.mass == "fine" and t >= self.window_chunks
+        fused = self.fused and attention and not fine_now
         # with a side stream the block masses (needed only by the update) are
         # computed there, off the attention's critical path
-        L.select(masses=self.side is None and self.mass == "coarse")
+        if not fused:
+            L.select(masses=self.side is None and self.mass == "coarse")
         self._attended = attention
         if attention:
             if fwd_events is not None:
                 fwd_events[0].record()
-            if self.mass == "fine" and t >= self.window_chunks:
+            if fused:
+                L.select_fwd()       # routing + attention, one launch where possible
+            elif fine_now:
                 L.fwd_mass()         # the update after this chunk ranks by these masses
             else:
                 L.fwd()
             if fwd_events is not None:
                 fwd_events[1].record()
+        if fused and self.side is None and self.mass == "coarse" and t >= self.window_chunks:
+            L.block_mass()           # the fused call leaves the masses to block_mass
         if self.side is None:
             self._side_work(L, t)
             return

@@ -198,6 +198,24 @@ int pbsa_attn_fwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, const
                   pbsa_stream_t stream);
 
 /*
+ * pbsa_select_attn_fwd - pbsa_select without masses followed by
+ * pbsa_attn_fwd (the same sections: coarse routing of each query block,
+ * then the hybrid attention over what it selected), with the same results
+ * bit for bit: sel, sel_count, kv->kbar_cur, o and lse (lse may be NULL).
+ * Where the problem allows (bf16, d = T = 128, C + topk <= 128, W <= 819,
+ * and no split of the forward) it is one launch in which each workgroup
+ * routes its own query block and then attends, so no launch boundary
+ * separates the two; otherwise the two launches of the separate calls.
+ * ws: the pbsa_select workspace (required), left as pbsa_select leaves it,
+ * so pbsa_block_mass can be given it afterwards.  fwd_ws: optional, as the
+ * workspace of pbsa_attn_fwd (it decides whether the forward splits).
+ * Calls that share a workspace must not overlap in time.
+ */
+int pbsa_select_attn_fwd(const pbsa_problem *p, const void *q, const pbsa_kv *kv, int32_t *sel,
+                         int32_t *sel_count, void *o, float *lse, void *ws, size_t ws_bytes,
+                         void *fwd_ws, size_t fwd_ws_bytes, pbsa_stream_t stream);
+
+/*
  * pbsa_attn_bwd - gradients through the fixed block mask (the trainable
  * sparse attention of the paper's title; selection is not differentiated).
  * With P the forward weights (recomputed from lse), D_r = <dO_r, O_r>,

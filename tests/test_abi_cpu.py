@@ -139,6 +139,19 @@ def test_entry_points_reject_before_launch():
                             need, None) == -1
     assert L.pbsa_fine_mass(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, fake, fake, fake,
                             need - 1, None) == -5
+    # select + forward in one call: o and the select workspace required,
+    # an optional forward workspace must be aligned
+    need = L.pbsa_workspace_size(ctypes.byref(p), P.PBSA_OP_SELECT)
+    assert L.pbsa_select_attn_fwd(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, None, fake,
+                                  fake, need, None, 0, None) == -1
+    assert L.pbsa_select_attn_fwd(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, fake,
+                                  None, 0, None, 0, None) == -5
+    assert L.pbsa_select_attn_fwd(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, fake,
+                                  fake, need - 1, None, 0, None) == -5
+    assert L.pbsa_select_attn_fwd(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, fake,
+                                  fake, need, fake + 8, 1 << 30, None) == -4
+    assert L.pbsa_select_attn_fwd(ctypes.byref(p), fake, ctypes.byref(kv2), None, fake, fake, fake,
+                                  fake, need, None, 0, None) == -1
     # fused forward + mass: lse, both mass buffers and the workspace required
     need = L.pbsa_workspace_size(ctypes.byref(p), P.PBSA_OP_FWD_MASS)
     assert L.pbsa_attn_fwd_mass(ctypes.byref(p), fake, ctypes.byref(kv2), fake, fake, fake, None, fake,

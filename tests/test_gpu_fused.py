@@ -1,0 +1,122 @@
+"""pbsa_select_attn_fwd (routing + attention in one call) against
+pbsa_select (no masses) followed by pbsa_attn_fwd, through the C ABI: the
+same selection, key means, workspace scores, outputs and LSE, bit for bit.
+Problems with d = T = 128 in bf16, C + topk <= 128 and no split of the
+forward take the one-launch kernel; the rest take the two launches.  The
+two-call results themselves are checked against the oracle elsewhere."""
+import sys
+
+import pytest
+import torch
+
+import pbsa_synth as syn
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from block_sparse_attention_20_amd.layer import PBSALayer
+    from block_sparse_attention_20_amd import pbsa as P
+
+from test_gpu_parity import CASES
+
+OUT_KEYS = ("sel", "sel_count", "kbar_cur", "o", "lse")
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _two_calls_then_fused(shape, st, ws_fwd):
+    """Outputs and select workspace of select + fwd, then of select_fwd on the
+    same layer with every output poisoned first."""
+    L = PBSALayer(shape.B, shape.H, shape.d, shape.T, shape.Nq, shape.W, shape.C, shape.topk,
+                  dtype=shape.dtype, device="cuda", ws_fwd=ws_fwd).load(st)
+    L.ws_select.fill_(0xAB)  # parts no call writes (the current-chunk scores) stay equal
+    L.select(masses=False)
+    L.fwd()
+    torch.cuda.synchronize()
+    ref = {k: L.t[k].clone() for k in OUT_KEYS}
+    ref_ws = L.ws_select.clone()
+    L.t["o"].fill_(float("nan"))
+    L.t["lse"].fill_(float("nan"))
+    L.t["kbar_cur"].fill_(float("nan"))
+    L.t["sel_count"].fill_(-7)
+    if shape.topk > 0:
+        L.t["sel"].fill_(-7)
+    L.ws_select.fill_(0xAB)
+    L.select_fwd()
+    torch.cuda.synchronize()
+    return L, ref, ref_ws
+
+
+def _assert_same(L, ref, ref_ws, what):
+    for k in OUT_KEYS:
+        assert torch.equal(L.t[k], ref[k]), (what, k)
+    assert torch.equal(L.ws_select, ref_ws), (what, "select workspace")
+    assert L.status_bits() == 0, what
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("with_fwd_ws", [False, True])
+def test_select_attn_fwd_equals_two_calls(name, with_fwd_ws):
+    shape, kw = CASES[name]
+    _log(f"case {name} fwd_ws={with_fwd_ws}")
+    st = syn.make_state(shape, 31, pad_value=float("nan"), **kw)
+    L, ref, ref_ws = _two_calls_then_fused(shape, st, "own" if with_fwd_ws else None)
+    _assert_same(L, ref, ref_ws, name)
+    # the masses pbsa_block_mass forms from the fused call's workspace
+    if shape.C + shape.W > 0:
+        L.block_mass()
+        torch.cuda.synchronize()
+        m = {k: L.t[k].clone() for k in ("mass_pool", "mass_win")}
+        L.select(masses=True)
+        torch.cuda.synchronize()
+        for k in ("mass_pool", "mass_win"):
+            assert torch.equal(L.t[k], m[k]), (name, k)
+
+
+@pytest.mark.parametrize("unscaled", [False, True])
+def test_select_attn_fwd_wan_chunk(unscaled):
+    """The Wan chunk (12 heads x 37 query blocks: one launch, no split) in
+    the layer configuration the rollout uses, with and without a forward
+    workspace (too many query blocks to split either way)."""
+    shape = syn.WAN_CHUNK
+    for ws_fwd in (None, "own"):
+        _log(f"wan chunk unscaled={unscaled} fwd_ws={ws_fwd}")
+        st = syn.wan_chunk_state(1, unscaled=unscaled)
+        L, ref, ref_ws = _two_calls_then_fused(shape, st, ws_fwd)
+        _assert_same(L, ref, ref_ws, f"wan chunk {ws_fwd}")
+
+
+def test_select_attn_fwd_bad_pool_count_is_flagged():
+    """A pool_count above C is clamped and flagged by the fused call as by
+    the separate ones, with the same outputs."""
+    shape, kw = CASES["bf16_d128_T128_small"]
+    st = syn.make_state(shape, 5, **kw)
+    outs = []
+    for fused in (False, True):
+        L = PBSALayer(shape.B, shape.H, shape.d, shape.T, shape.Nq, shape.W, shape.C, shape.topk,
+                      device="cuda", ws_fwd=None).load(st)
+        L.t["pool_count"].fill_(99)
+        if fused:
+            L.select_fwd()
+        else:
+            L.select(masses=False)
+            L.fwd()
+        torch.cuda.synchronize()
+        assert L.status_bits() & P.PBSA_STATUS_POOL_COUNT
+        outs.append({k: L.t[k].clone() for k in OUT_KEYS})
+    for k in OUT_KEYS:
+        assert torch.equal(outs[0][k], outs[1][k]), k
+
+
+def test_select_attn_fwd_requires_select_workspace():
+    shape, kw = CASES["bf16_d128_T128_small"]
+    st = syn.make_state(shape, 5, **kw)
+    L = PBSALayer(shape.B, shape.H, shape.d, shape.T, shape.Nq, shape.W, shape.C, shape.topk,
+                  device="cuda", ws_fwd=None).load(st)
+    t = L.t
+    with pytest.raises(P.PBSAError) as e:
+        P.pbsa_select_attn_fwd(L.prob, t["q"], L.kv, t["sel"], t["sel_count"], t["o"], t["lse"], None)
+    assert e.value.code == P.PBSA_ERR_WORKSPACE

@@ -124,6 +124,40 @@ def test_rollout_side_stream_overlap_is_bitwise_identical():
         assert torch.equal(a, b)
 
 
+def test_rollout_fused_select_attn_is_bitwise_identical():
+    """The rollout's routing + attention through pbsa_select_attn_fwd (one
+    launch per layer at the Wan shape) against pbsa_select then
+    pbsa_attn_fwd: outputs, selections and cache state equal bit for bit
+    over 2 layers and 5 chunks (pool filling at chunks 2-3), with the side
+    stream."""
+    C = 16
+    shape = syn.Shape(B=1, H=12, d=128, T=128, Nq=4680, W=0, C=C, topk=16)
+    outs = {}
+    for fused in (False, True):
+        ro = Rollout(2, 1, 12, 128, 128, 4680, C, 16, overlap=True, fused=fused)
+        res = []
+        for t in range(5):
+            for l in range(2):
+                u = syn.rollout_direction(3, l, t, 128)
+                ch = syn.make_chunk(shape, syn.rollout_seed(3, l, t), u, sigma=1 / math.sqrt(128),
+                                    shift=1.5, n_planted=8)
+                ro.set_inputs(l, ch["q"].cuda(), ch["k"].cuda(), ch["v"].cuda())
+                ro.run_layer(l)
+                L = ro.layers[l]
+                res += [L.t["o"].clone(), L.t["lse"].clone(), L.t["sel"].clone(),
+                        L.t["sel_count"].clone()]
+            ro.advance()
+        ro.sync_side()
+        torch.cuda.synchronize()
+        for L in ro.layers:
+            res += [L.t[k].clone() for k in ("pool_id", "pool_count", "k_pool", "kbar_pool",
+                                              "win_id", "kbar_win", "k_win")]
+        outs[fused] = res
+        _log(f"  fused={fused} pool {int(ro.layers[0].t['pool_count'][0, 0])}")
+    for i, (a, b) in enumerate(zip(outs[False], outs[True])):
+        assert torch.equal(a, b), i
+
+
 def test_rollout_work_is_flat_once_pool_full():
     """Pool empty for chunks 0-2, QB blocks after chunk 3's update... full (C)
     from chunk 4 on; every query block selects k window blocks once the
