@@ -39,15 +39,15 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 
-# HBM traffic of one forward launch on this workload, from two rocprofv3
+# HBM traffic of one routing + forward launch on this workload, from two rocprofv3
 # --pmc passes (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by
 # what the same counter reads for a copy kernel of known size (the window
 # append: 28,302 KiB read and 28,302 KiB written per launch; it reads back
 # FETCH 14,167 KiB, WRITE 28,304 KiB).  Valid only for the kernel source it
 # was measured on (sha1 over FWD_SOURCES below); reported as null once those
 # sources change.
-FWD_TRAFFIC = {"src_sha1": "86861af3fc5c657cfa3b957bd09563154aa2fb7c",
-               "fetch_kib": 59728.0, "write_kib": 14260.0,
+FWD_TRAFFIC = {"src_sha1": "4e6196473e832c994b9ac7579f21a8f3b4707f01",
+               "fetch_kib": 68140.8, "write_kib": 16943.4,
                "fetch_scale": 28302.0 / 14166.5, "write_scale": 28302.0 / 28304.3}
 
 
@@ -76,12 +76,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_rollout(n_layers, device):
+def build_rollout(n_layers, device, side_group=5):
     import pbsa_synth as syn
     from block_sparse_attention_20_amd.rollout import Rollout
     s = syn.WAN_CHUNK
     ro = Rollout(n_layers, s.B, s.H, s.d, s.T, s.Nq, s.C, s.topk, window_chunks=2, device=device,
-                 overlap=True)
+                 overlap=True, side_group=side_group)
     for l in range(n_layers):
         st = syn.wan_chunk_state(l, device=device)
         ro.layers[l].load(st)
@@ -193,7 +193,7 @@ def train_step(torch, steps=5, warmup=2, device="cuda"):
             "bwd_flop_convention": "10*d per attended (row, token) pair, QK^T recompute included"}
 
 
-def rollout_bench(n_chunks, config_id, torch, n_layers=30, device="cuda"):
+def rollout_bench(n_chunks, config_id, torch, n_layers=30, device="cuda", side_group=5):
     """Streaming rollout in the Wan shape: n_chunks chunks of 4680 tokens,
     30 layers with independent state, window of the two previous chunks,
     pool capped at 64 blocks, Top-C update after every chunk.  Each new chunk
@@ -207,7 +207,7 @@ def rollout_bench(n_chunks, config_id, torch, n_layers=30, device="cuda"):
     C = syn.ROLLOUT_POOL_CAP
     shape = syn.Shape(B=s.B, H=s.H, d=s.d, T=s.T, Nq=s.Nq, W=0, C=C, topk=s.topk)
     ro = Rollout(n_layers, s.B, s.H, s.d, s.T, s.Nq, C, s.topk, window_chunks=2, device=device,
-                 overlap=True)
+                 overlap=True, side_group=side_group)
     sigma = 1 / math.sqrt(s.d)
     ms, gflop, pool = [], [], []
     for t in range(n_chunks):
@@ -623,6 +623,8 @@ def main():
     ap.add_argument("--layers", type=int, default=30)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle forward work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--side-group", type=int, default=5,
+                    help="layers whose update + append go to the side stream together")
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--no-rollout", action="store_true", help="skip the 20 s / 1 min rollouts")
     ap.add_argument("--sweep", action="store_true",
@@ -657,7 +659,7 @@ def main():
         print(json.dumps({"mass_compare": mass_compare(torch, device=dev)}), flush=True)
         return
     log(f"building 30-layer state ({args.layers} layers)")
-    ro = build_rollout(args.layers, dev)
+    ro = build_rollout(args.layers, dev, args.side_group)
     torch.cuda.synchronize()
     log("timing")
     ms, fwd_samples, flops_layer, step_ms = time_steps(ro, args.steps, args.warmup, torch)
@@ -700,9 +702,9 @@ def main():
         out["train"] = train_step(torch)
     if not args.no_rollout:
         log("rollout 27 chunks (20 s)")
-        out["rollout_20s"] = rollout_bench(27, 2, torch)
+        out["rollout_20s"] = rollout_bench(27, 2, torch, side_group=args.side_group)
         log("rollout 80 chunks (1 min)")
-        out["rollout_1min"] = rollout_bench(80, 3, torch)
+        out["rollout_1min"] = rollout_bench(80, 3, torch, side_group=args.side_group)
     if not args.no_cpu_baseline:
         log("cpu baseline")
         out["cpu_baseline"] = cpu_baseline(ro, args.cpu_budget, torch)

@@ -31,7 +31,9 @@ are needed by the next *chunk*.  The side stream waits for the layer's
 forward (the update rewrites pool slots the forward reads); the next chunk's
 select of the layer (which rewrites the scores the masses are computed from)
 and the next write of its inputs wait for the side work.  Both streams keep
-the default priority.
+the default priority.  ``side_group`` layers share one launch of side work
+(and one event on each stream); every layer's side work is launched by the
+time the chunk advances.
 """
 from __future__ import annotations
 
@@ -50,7 +52,7 @@ class Rollout:
     def __init__(self, n_layers: int, B: int, H: int, d: int, T: int, Nq: int, C: int, topk: int,
                  n_sink: int = 0, window_chunks: int = 2, dtype=torch.bfloat16, scale: float = 0.0,
                  device="cuda", overlap: bool = False, mass: str = "coarse",
-                 shared_pool: bool = False, fused: bool = True):
+                 shared_pool: bool = False, fused: bool = True, side_group: int = 1):
         if mass not in ("coarse", "fine"):
             raise ValueError(f"mass must be 'coarse' or 'fine', not {mass!r}")
         self.mass = mass
@@ -76,14 +78,46 @@ class Rollout:
                         for p in range(window_chunks)]
         self.t = 0
         self.side = torch.cuda.Stream(device=device) if overlap else None
-        self.ev_fwd = [torch.cuda.Event() for _ in range(n_layers)] if overlap else None
-        self.ev_side = [torch.cuda.Event() for _ in range(n_layers)] if overlap else None
-        self.side_pending = [False] * n_layers
+        # side_group: layers whose side work goes to the side stream together,
+        # behind one event on each stream (fewer event packets between the
+        # forwards on the critical stream)
+        if side_group < 1:
+            raise ValueError("side_group must be >= 1")
+        self.side_group = side_group
+        self._pend: List[int] = []       # layers run whose side work is not launched yet
+        self._side_ev: List[Optional[torch.cuda.Event]] = [None] * n_layers
+        self._attended = [True] * n_layers
 
     def _wait_side(self, layer: int):
-        if self.side is not None and self.side_pending[layer]:
-            torch.cuda.current_stream().wait_event(self.ev_side[layer])
-            self.side_pending[layer] = False
+        """The current stream waits for the side work that covers ``layer``
+        (and so for every layer launched with it)."""
+        if self.side is None:
+            return
+        if layer in self._pend:
+            self._flush_side()
+        ev = self._side_ev[layer]
+        if ev is not None:
+            torch.cuda.current_stream().wait_event(ev)
+            for l, e in enumerate(self._side_ev):
+                if e is ev:
+                    self._side_ev[l] = None
+
+    def _flush_side(self):
+        """Launch the side work of the pending layers on the side stream,
+        after everything enqueued so far on the current stream."""
+        if not self._pend:
+            return
+        ev_fwd = torch.cuda.Event()
+        ev_fwd.record()
+        ev_side = torch.cuda.Event()
+        with torch.cuda.stream(self.side):
+            self.side.wait_event(ev_fwd)
+            for l in self._pend:
+                self._side_work(self.layers[l], self.t, self._attended[l])
+            ev_side.record(self.side)
+        for l in self._pend:
+            self._side_ev[l] = ev_side
+        self._pend = []
 
     def first_slot(self, chunk: int) -> int:
         return (chunk % self.window_chunks) * self.QB
@@ -108,7 +142,7 @@ class Rollout:
         # computed there, off the attention's critical path
         if not fused:
             L.select(masses=self.side is None and self.mass == "coarse")
-        self._attended = attention
+        self._attended[layer] = attention
         if attention:
             if fwd_events is not None:
                 fwd_events[0].record()
@@ -123,18 +157,15 @@ class Rollout:
         if fused and self.side is None and self.mass == "coarse" and t >= self.window_chunks:
             L.block_mass()           # the fused call leaves the masses to block_mass
         if self.side is None:
-            self._side_work(L, t)
+            self._side_work(L, t, attention)
             return
-        self.ev_fwd[layer].record()
-        with torch.cuda.stream(self.side):
-            self.side.wait_event(self.ev_fwd[layer])
-            self._side_work(L, t)
-            self.ev_side[layer].record(self.side)
-        self.side_pending[layer] = True
+        self._pend.append(layer)
+        if len(self._pend) >= self.side_group or layer == len(self.layers) - 1:
+            self._flush_side()
 
-    def _side_work(self, L, t):
+    def _side_work(self, L, t, attended):
         if t >= self.window_chunks:
-            if self.mass == "fine" and self._attended:
+            if self.mass == "fine" and attended:
                 pass                 # pbsa_attn_fwd_mass wrote the masses
             elif self.side is not None or self.mass == "fine":
                 L.block_mass()       # coarse masses from the select scores
@@ -143,6 +174,8 @@ class Rollout:
 
     def sync_side(self):
         """Make the current stream wait for every layer's side work."""
+        if self.side is not None:
+            self._flush_side()
         for l in range(len(self.layers)):
             self._wait_side(l)
 
@@ -152,6 +185,8 @@ class Rollout:
         self.advance()
 
     def advance(self):
+        if self.side is not None:
+            self._flush_side()   # side work of this chunk's layers, before t moves on
         self.t += 1
 
     # -- checkpoint / resume ---------------------------------------------------

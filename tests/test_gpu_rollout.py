@@ -101,13 +101,14 @@ def test_rollout_checkpoint_resume_bitwise():
 
 
 def test_rollout_side_stream_overlap_is_bitwise_identical():
-    """Update + append on a side stream (overlapped with the next layers)
-    gives exactly the serial result, over several layers and chunks."""
+    """Update + append on a side stream (overlapped with the next layers),
+    per layer or two layers at a time, gives exactly the serial result, over
+    several layers and chunks."""
     shape = syn.Shape(B=1, H=2, d=128, T=128, Nq=300, W=0, C=4, topk=3)
     chunks = make_chunks(shape, 6)
     outs = {}
-    for overlap in (False, True):
-        ro = Rollout(3, 1, 2, 128, 128, 300, 4, 3, overlap=overlap)
+    for overlap, group in ((False, 1), (True, 1), (True, 2)):
+        ro = Rollout(3, 1, 2, 128, 128, 300, 4, 3, overlap=overlap, side_group=group)
         res = []
         for ch in chunks:
             for l in range(3):
@@ -119,9 +120,10 @@ def test_rollout_side_stream_overlap_is_bitwise_identical():
         torch.cuda.synchronize()
         res.append(ro.layers[2].t["k_pool"].clone())
         res.append(ro.layers[1].t["pool_id"].clone())
-        outs[overlap] = res
-    for a, b in zip(outs[False], outs[True]):
-        assert torch.equal(a, b)
+        outs[(overlap, group)] = res
+    for key in ((True, 1), (True, 2)):
+        for a, b in zip(outs[(False, 1)], outs[key]):
+            assert torch.equal(a, b), key
 
 
 def test_rollout_fused_select_attn_is_bitwise_identical():
@@ -134,7 +136,8 @@ def test_rollout_fused_select_attn_is_bitwise_identical():
     shape = syn.Shape(B=1, H=12, d=128, T=128, Nq=4680, W=0, C=C, topk=16)
     outs = {}
     for fused in (False, True):
-        ro = Rollout(2, 1, 12, 128, 128, 4680, C, 16, overlap=True, fused=fused)
+        ro = Rollout(2, 1, 12, 128, 128, 4680, C, 16, overlap=True, fused=fused,
+                     side_group=2 if fused else 1)
         res = []
         for t in range(5):
             for l in range(2):
