@@ -114,13 +114,22 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// sel_lds: the query block's selection already in LDS (n_sel entries; the
-// fused select + forward), else nullptr (read from a.sel / a.sel_count).
-template <int D, int BT, bool MASS>
+// No routing: the selection is read from a.sel / a.sel_count.
+struct NoRoute {
+  __device__ int operator()() const { return 0; }
+};
+
+// route (the fused select + forward): routes the query block into sel_lds,
+// leaves the window and pool slot lengths in lens ([W] then [C]) and
+// returns the selection's size; it runs after this workgroup's query
+// fragments are in flight and may use K1 and V1 (the first tile goes to K0
+// and V0, issued once the routing is done).
+template <int D, int BT, bool MASS, typename Route = NoRoute>
 __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh, uint16_t *K0,
                                             uint16_t *K1, uint16_t *V0, uint16_t *V1, int wg, int item,
                                             int j0, int j1, const int32_t *sel_lds = nullptr,
-                                            int n_sel = 0) {
+                                            Route route = Route{}, const int *lens = nullptr) {
+  constexpr bool ROUTED = !std::is_same<Route, NoRoute>::value;
   constexpr int NW = BT / 32;  // waves; wave w owns query rows [32w, 32w+32)
   constexpr int TT = kTile;
   using G = DmaGeom<D, TT, NW>;
@@ -136,16 +145,13 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  int n_pool, sc, nb;
-  if (sel_lds) {
+  int n_pool, sc = 0, nb = 0;
+  if constexpr (ROUTED) {
     n_pool = a.pool_count[bh];
-    n_pool = max(0, min(n_pool, a.C));  // the routing has flagged a bad count
-    sc = n_sel;
-    nb = n_pool + sc + a.QB;
+    n_pool = max(0, min(n_pool, a.C));  // the routing flags a bad count
   } else {
     nb = clamp_counts(a, bh, i, n_pool, sc);
   }
-  const int jend = min(j1, nb);
 
   // this lane's query column, held as MFMA B fragments for the whole kernel
   const int qrow = i * BT + wave * 32 + l32;
@@ -173,7 +179,6 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
   // entries come first in the list, so the sum is still small there and the
   // difference loses little.
   float lprev = 0.f;
-  const int n_scored = n_pool + sc;
 
   // Per-lane LDS element offsets, fixed for the whole kernel.
   // K fragment (A of S^T): tile row tt*32 + l32, logical chunk 2kk + g.
@@ -194,15 +199,39 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, FwdLds<D, BT> &sh,
   uint32_t kdma[G::NVAR], vdma[G::NVAR];
   dma_lane_offsets<D, TT, NW, kSwzK>(lane, kdma);
   dma_lane_offsets<D, TT, NW, kSwzV>(lane, vdma);
-  __syncthreads();  // the previous segment of this workgroup is done with LDS
-  preload_list<D, BT>(a, bh, i, n_pool, sc, blist, t, 2 * BT, sel_lds);
-  __syncthreads();
+  // the previous segment of this workgroup is done with LDS (a routed
+  // segment is the workgroup's first: no wait, so the query fragments stay
+  // in flight through the routing)
+  if constexpr (!ROUTED) __syncthreads();
+  if constexpr (ROUTED) {
+    sc = route();
+    nb = n_pool + sc + a.QB;
+  }
+  const int jend = min(j1, nb);
+  const int n_scored = n_pool + sc;
 
   // tile stream: (block j, half h); tile rows = min(64, len_j - 64 h)
   int j = j0, h = 0;
-  const uint16_t *kb, *vb;
+  const uint16_t *kb = nullptr, *vb = nullptr;
   int blen = 0, tlen = 0;
-  if (j0 < jend) {
+  bool first_issued = false;
+  if constexpr (ROUTED) {
+    // a non-empty pool heads the list: its first tile moves while the list
+    // is resolved (the routing left the slot lengths in LDS)
+    if (j0 == 0 && n_pool > 0) {
+      const size_t off = (bh * a.C) * (size_t)(BT * D);
+      kb = (const uint16_t *)a.k_pool + off;
+      vb = (const uint16_t *)a.v_pool + off;
+      blen = max(0, min(__builtin_amdgcn_readfirstlane(lens[a.W]), BT));
+      tlen = min(TT, blen);
+      TileDma<D, TT, NW>::tile(Kb[0], kb, tlen, wave, kdma);
+      TileDma<D, TT, NW>::tile(Vb[0], vb, tlen, wave, vdma);
+      first_issued = true;
+    }
+  }
+  preload_list<D, BT>(a, bh, i, n_pool, sc, blist, t, 2 * BT, sel_lds, lens);
+  __syncthreads();
+  if (j0 < jend && !first_issued) {
     list_block<D, BT>(a, blist, bh, i, n_pool, sc, j0, kb, vb, blen);
     tlen = min(TT, blen);
     TileDma<D, TT, NW>::tile(Kb[0], kb, tlen, wave, kdma);
@@ -433,9 +462,12 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void attn_fwd_bf16_kerne
 // score rows are bit-identical), then attends with the selection it holds
 // in LDS.  The routing's scratch borrows the second K and V tile buffers,
 // which the walk first fills during the first tile (after the routing is
-// done); it needs 16 KB of each: 2 x 256 x 8 floats of partial sums, and
-// 20 B per window slot (W <= 819).  The block list takes at most 128
-// entries (C + topk <= 128), all resolved from LDS.
+// done); it needs 16 KB of each: 2 x 256 x 8 floats of partial sums (then
+// the slot lengths), and 20 B per window slot (W <= 819).  The block list
+// takes at most 128 entries (C + topk <= 128), all resolved from LDS.  The
+// current block's key mean, which nothing in the launch reads, is taken at
+// the end (its rows are in L2 by then), so the routing's HBM burst holds
+// only the query rows.
 constexpr int kFusedMaxW = (kTile * 128 * 2) / 20;
 
 template <int D, int BT>
@@ -449,12 +481,31 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_fwd_sel_bf16_kernel(FwdArgs a,
   __shared__ float both[256];
   __shared__ int nvalid, wcnt[4], n_sel;
   __shared__ int32_t sel_lds[kMaxList];
+  __shared__ uint64_t kout[2];  // where the key mean goes (kept out of scalar registers)
   int wg;
   item_of_block(a, wg);
   if (wg >= a.n_items) return;
-  const SelLds L{qv, reinterpret_cast<float *>(K1), both, V1, &nvalid, wcnt, sel_lds, &n_sel};
-  select_query_block<uint16_t>(s, wg % a.QB, (size_t)(wg / a.QB), L);
-  fwd_segment<D, BT, false>(a, sh, K0, K1, V0, V1, wg, wg, 0, a.NB, sel_lds, n_sel);
+  const int i = wg % a.QB;
+  const size_t bh = wg / a.QB;
+  if (threadIdx.x == 0) {
+    kout[0] = reinterpret_cast<uint64_t>(s.kbar_cur + (bh * a.QB + i) * D);
+    kout[1] = reinterpret_cast<uint64_t>(s.kbarc_out + (bh * a.QB + i) * D);
+  }
+  int *lens = reinterpret_cast<int *>(K1);
+  const SelLds L{qv, reinterpret_cast<float *>(K1), both, V1, &nvalid, wcnt, sel_lds, &n_sel, lens};
+  auto route = [&]() -> int {
+    select_query_block<uint16_t, false>(s, i, bh, L);
+    return n_sel;
+  };
+  fwd_segment<D, BT, false>(a, sh, K0, K1, V0, V1, wg, wg, 0, a.NB, sel_lds, route, lens);
+  // the walk's last DMA (zeros into the idle buffer) has landed before K1
+  // is reused
+  PBSA_WAIT_VM(0);
+  __syncthreads();
+  float *kbar = reinterpret_cast<float *>(kout[0]);
+  float *kbarc = reinterpret_cast<float *>(kout[1]);
+  key_block_mean<uint16_t>((const uint16_t *)a.k_cur + (bh * a.Nq + (size_t)i * BT) * D,
+                           min(BT, a.Nq - i * BT), D, kbar, kbarc, reinterpret_cast<float *>(K1), both);
 }
 
 // Merge of the split pieces, one workgroup per (query block, 32 of the d

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void score_topk_kernel(SelArgs<TIn> s) {
   __shared__ float both[256];
   __shared__ int nvalid_sh;
   __shared__ int wcnt[4];
-  const SelLds L{qv, red, both, smem, &nvalid_sh, wcnt, nullptr, nullptr};
+  const SelLds L{qv, red, both, smem, &nvalid_sh, wcnt, nullptr, nullptr, nullptr};
   select_query_block<TIn>(s, blockIdx.x, (size_t)blockIdx.z * s.H + blockIdx.y, L);
 }
 

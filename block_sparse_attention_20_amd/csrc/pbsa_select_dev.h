@@ -16,54 +16,56 @@
 
 namespace pbsa {
 
-// Means of the first n rows of two [rows, d] blocks a and b (row stride d)
-// at once, so that both blocks' loads are in flight together; fp32 sums in
-// a fixed order.  256 threads, 16-byte loads; red: LDS, >= 2*256*8 floats.
-// Threads [0, d) write out_a[t], threads [d, 2d) out_b[t - d]; both means
-// also go to both[0, 2d) (LDS).
-template <typename TIn>
+// Means of the first n rows of NBLK [rows, d] blocks a (and b) (row stride
+// d), both blocks' loads in flight together; fp32 sums in a fixed order,
+// the same for a block averaged alone or with another.  256 threads, 16-byte
+// loads; red: LDS, >= NBLK*256*8 floats.  Threads [0, d) write out_a[t],
+// threads [d, 2d) out_b[t - d]; the means also go to both[0, NBLK*d) (LDS,
+// for the caller after a sync).
+template <typename TIn, int NBLK = 2>
 __device__ void two_block_means(const TIn *__restrict__ a, const TIn *__restrict__ b, int n, int d,
                                 float *out_a, float *out_b, float *red, float *both) {
   constexpr int E = 16 / sizeof(TIn);
   const int tpr = d / E, rpp = 256 / tpr;
   const int t = threadIdx.x;
   const int rg = t / tpr, cg = t % tpr;
-  float acc[2][E];
+  const TIn *src[2] = {a, b};
+  float acc[NBLK][E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[0][e] = acc[1][e] = 0.f;
+  for (int k = 0; k < NBLK; ++k)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[k][e] = 0.f;
 #pragma unroll 8
   for (int r = rg; r < n; r += rpp) {
-    const u32x4 va = *reinterpret_cast<const u32x4 *>(a + (size_t)r * d + cg * E);
-    const u32x4 vb = *reinterpret_cast<const u32x4 *>(b + (size_t)r * d + cg * E);
-    if constexpr (sizeof(TIn) == 2) {
+    u32x4 v[NBLK];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[0][2 * e] += bflo(va[e]);
-        acc[0][2 * e + 1] += bfhi(va[e]);
-        acc[1][2 * e] += bflo(vb[e]);
-        acc[1][2 * e + 1] += bfhi(vb[e]);
-      }
-    } else {
+    for (int k = 0; k < NBLK; ++k) v[k] = *reinterpret_cast<const u32x4 *>(src[k] + (size_t)r * d + cg * E);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[0][e] += __uint_as_float(va[e]);
-        acc[1][e] += __uint_as_float(vb[e]);
+    for (int k = 0; k < NBLK; ++k) {
+      if constexpr (sizeof(TIn) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[k][2 * e] += bflo(v[k][e]);
+          acc[k][2 * e + 1] += bfhi(v[k][e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[k][e] += __uint_as_float(v[k][e]);
       }
     }
   }
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    red[rg * d + cg * E + e] = acc[0][e];
-    red[256 * 8 + rg * d + cg * E + e] = acc[1][e];
-  }
+  for (int k = 0; k < NBLK; ++k)
+#pragma unroll
+    for (int e = 0; e < E; ++e) red[k * 256 * 8 + rg * d + cg * E + e] = acc[k][e];
   __syncthreads();
-  if (t < 2 * d) {
+  if (t < NBLK * d) {
     const int c = t % d, w = t / d;
     float s = 0.f;
     for (int g = 0; g < rpp; ++g) s += red[w * 256 * 8 + g * d + c];
     const float v = n > 0 ? s / (float)n : 0.f;
     if (w == 0) out_a[c] = v; else out_b[c] = v;
-    both[t] = v;  // [a | b], for the caller (after a sync)
+    both[t] = v;
   }
 }
 
@@ -73,7 +75,7 @@ struct SelArgs {
   const TIn *q, *k_cur;
   float *qbar_out, *kbarc_out, *kbar_cur;
   const float *kbar_pool, *kbar_win;
-  const int32_t *pool_count, *win_len;
+  const int32_t *pool_count, *win_len, *pool_len;
   const int64_t *win_id;
   int32_t *sel, *sel_count;
   float *srow_out;
@@ -99,6 +101,7 @@ inline SelArgs<TIn> sel_args(const pbsa_problem &p, float scale, const void *q, 
   s.kbar_win = kv.kbar_win;
   s.pool_count = kv.pool_count;
   s.win_len = kv.win_len;
+  s.pool_len = kv.pool_len;
   s.win_id = kv.win_id;
   s.sel = sel;
   s.sel_count = sel_count;
@@ -127,6 +130,10 @@ struct SelLds {
   int *wcnt;       // [4]
   int32_t *sel_lds;  // optional [topk]: the selection, as written to sel
   int *n_sel_lds;    // optional [1]: its count
+  // optional [W + C]: the window slots' and pool slots' lengths, as read
+  // (unclamped), written over red once the means are done (needs
+  // W <= 4 * 256, C <= 256)
+  int *lens;
 };
 
 // 16 candidates per pass; 7 passes cover the 106 pool and window candidates
@@ -149,8 +156,9 @@ constexpr int kScorePasses = 7;
 //    Exact and order-independent, hence deterministic.  Scores enter the
 //    ranking as order keys (order_key; 0 = invalid slot), so the pairwise
 //    comparisons are branch free.
-// Ends with the workgroup synchronised.
-template <typename TIn>
+// KMEAN = false leaves kbar_cur_i and its workspace copy to key_block_mean
+// (the same bits, later).  Ends with the workgroup synchronised.
+template <typename TIn, bool KMEAN = true>
 __device__ __forceinline__ void select_query_block(const SelArgs<TIn> &s, int i, size_t bh,
                                                    const SelLds &L) {
   const int H = s.H, Nq = s.Nq, d = s.d, T = s.T, W = s.W, C = s.C, QB = s.QB, topk = s.topk;
@@ -170,26 +178,43 @@ __device__ __forceinline__ void select_query_block(const SelArgs<TIn> &s, int i,
     n_pool = max(0, min(n_pool, C));
   }
   int nv = 0;
-  for (int w = t; w < W; w += 256) {
+  int wl[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int w = t + 256 * u;
+    if (w < W) {
+      const int len = s.win_len[w];
+      if (len > T) set_status(s.status, PBSA_STATUS_WIN_LEN);
+      flag[w] = len > 0 ? 1 : 0;
+      nv += len > 0;
+      wid[w] = s.win_id[w];
+      wl[u] = len;
+    }
+  }
+  for (int w = t + 1024; w < W; w += 256) {
     const int len = s.win_len[w];
     if (len > T) set_status(s.status, PBSA_STATUS_WIN_LEN);
     flag[w] = len > 0 ? 1 : 0;
     nv += len > 0;
     wid[w] = s.win_id[w];
   }
+  const int pl = (L.lens && t < C) ? s.pool_len[bh * C + t] : 0;
   if (t == 0) nvalid_sh = 0;
   const int nj = C + W;                 // candidates scored here
   const int nrow = C + W + QB;          // score row length (current part: block mass)
   const int sub = lane >> 4, sl = lane & 15;
   const int per = d / 16;  // floats per lane (8 or 4)
   float *srow = s.srow_out + (bh * QB + i) * (size_t)nrow;
-  // one batch of candidate loads (the first kScorePasses * 16 candidates)
+  // one batch of candidate loads (the first kScorePasses * 16 candidates).
+  // Every stored slot's representative is loaded (in bounds whether or not
+  // the slot is valid), so the loads wait for no metadata; an invalid
+  // slot's score is replaced by -inf below.
   auto load_batch = [&](int base, f32x4 (&k0)[kScorePasses], f32x4 (&k1)[kScorePasses],
                         bool (&ok)[kScorePasses]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ps = 0; ps < kScorePasses; ++ps) {
       const int j = base + ps * 16 + sub;
-      const float *kb = s.kbar_pool;
+      const float *kb = nullptr;
       bool valid = false;
       if (j < C) {
         valid = j < n_pool;
@@ -201,7 +226,7 @@ __device__ __forceinline__ void select_query_block(const SelArgs<TIn> &s, int i,
       ok[ps] = valid;
       k0[ps] = f32x4{0.f, 0.f, 0.f, 0.f};
       k1[ps] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (valid) {
+      if (j < nj) {
         k0[ps] = *reinterpret_cast<const f32x4 *>(kb + sl * per);
         if (per == 8) k1[ps] = *reinterpret_cast<const f32x4 *>(kb + sl * per + 4);
       }
@@ -214,13 +239,22 @@ __device__ __forceinline__ void select_query_block(const SelArgs<TIn> &s, int i,
   // the block's own means (Q -> qbar, K -> kbar_cur)
   {
     const int r0 = i * T, n = min(T, Nq - r0);
-    two_block_means<TIn>(s.q + (bh * Nq + r0) * d, s.k_cur + (bh * Nq + r0) * d, n, d, qv,
-                         s.kbar_cur + (bh * QB + i) * d, L.red, L.both);
+    if constexpr (KMEAN)
+      two_block_means<TIn>(s.q + (bh * Nq + r0) * d, s.k_cur + (bh * Nq + r0) * d, n, d, qv,
+                           s.kbar_cur + (bh * QB + i) * d, L.red, L.both);
+    else
+      two_block_means<TIn, 1>(s.q + (bh * Nq + r0) * d, nullptr, n, d, qv, nullptr, L.red, L.both);
   }
   __syncthreads();
   if (t < d) {
     s.qbar_out[(bh * QB + i) * d + t] = qv[t];
-    s.kbarc_out[(bh * QB + i) * d + t] = L.both[d + t];
+    if constexpr (KMEAN) s.kbarc_out[(bh * QB + i) * d + t] = L.both[d + t];
+  }
+  if (L.lens) {  // red is dead from here on
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (t + 256 * u < W) L.lens[t + 256 * u] = wl[u];
+    if (t < C) L.lens[W + t] = pl;
   }
   for (int o = 32; o > 0; o >>= 1) nv += __shfl_xor(nv, o);
   if (lane == 0) atomicAdd(&nvalid_sh, nv);
@@ -301,6 +335,19 @@ __device__ __forceinline__ void select_query_block(const SelArgs<TIn> &s, int i,
     s.sel_count[bh * QB + i] = n_sel;
     if (L.n_sel_lds) *L.n_sel_lds = n_sel;
   }
+  __syncthreads();
+}
+
+// kbar_cur_i and its workspace copy, as select_query_block<TIn, true>
+// computes them (same loads and summation order), from the current block's
+// K rows.  red: >= 256*8 floats of LDS, both: >= d floats.  Ends with the
+// workgroup synchronised.
+template <typename TIn>
+__device__ __forceinline__ void key_block_mean(const TIn *k_rows, int n, int d, float *kbar_out,
+                                               float *kbarc_out, float *red, float *both) {
+  two_block_means<TIn, 1>(k_rows, nullptr, n, d, kbar_out, nullptr, red, both);
+  __syncthreads();
+  if (threadIdx.x < d) kbarc_out[threadIdx.x] = both[threadIdx.x];
   __syncthreads();
 }
 

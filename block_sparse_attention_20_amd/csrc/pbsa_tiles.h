@@ -195,18 +195,20 @@ struct BlockList {
 };
 
 // selrow: the query block's selected window slots; nullptr = its row of
-// a.sel.
+// a.sel.  lens: the window slots' lengths then this (b, h)'s pool slots'
+// (as in a.win_len / a.pool_len); nullptr = read them there.
 template <int D, int BT, typename Args>
 __device__ __forceinline__ void preload_list(const Args &a, size_t bh, int i, int n_pool, int sc,
                                              BlockList &bl, int t, int nt,
-                                             const int32_t *selrow = nullptr) {
+                                             const int32_t *selrow = nullptr,
+                                             const int *lens = nullptr) {
   const int n = min(n_pool + sc, kMaxList);
   for (int j = t; j < n; j += nt) {
     int64_t off;
     int len, win = 0;
     if (j < n_pool) {
       off = (int64_t)(bh * a.C + j) * (BT * D);
-      len = a.pool_len[bh * a.C + j];
+      len = lens ? lens[a.W + j] : a.pool_len[bh * a.C + j];
     } else {
       const int w = selrow ? selrow[j - n_pool] : a.sel[(bh * a.QB + i) * (size_t)a.topk + (j - n_pool)];
       win = 1;
@@ -216,7 +218,7 @@ __device__ __forceinline__ void preload_list(const Args &a, size_t bh, int i, in
         len = 0;
       } else {
         off = (int64_t)(bh * a.W + w) * (BT * D);
-        len = a.win_len[w];
+        len = lens ? lens[w] : a.win_len[w];
       }
     }
     if (len < 0 || len > BT) {
