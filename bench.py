@@ -46,8 +46,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # FETCH 14,167 KiB, WRITE 28,304 KiB).  Valid only for the kernel source it
 # was measured on (sha1 over FWD_SOURCES below); reported as null once those
 # sources change.
-FWD_TRAFFIC = {"src_sha1": "4e6196473e832c994b9ac7579f21a8f3b4707f01",
-               "fetch_kib": 68140.8, "write_kib": 16943.4,
+FWD_TRAFFIC = {"src_sha1": "89e08321aac3f3077e54ef370930fe6418fa8479",
+               "fetch_kib": 64343.8, "write_kib": 15154.6,
                "fetch_scale": 28302.0 / 14166.5, "write_scale": 28302.0 / 28304.3}
 
 

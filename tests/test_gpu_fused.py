@@ -89,6 +89,19 @@ def test_select_attn_fwd_wan_chunk(unscaled):
         _assert_same(L, ref, ref_ws, f"wan chunk {ws_fwd}")
 
 
+@pytest.mark.parametrize("W,C,topk", [(900, 4, 8), (200, 100, 40)])
+def test_select_attn_fwd_past_the_one_launch_limits(W, C, topk):
+    """A window past the routing scratch (W > 819) and a list past the 128
+    entries held in LDS (C + topk > 128) take the two launches inside the
+    call: still the same results as the separate calls."""
+    shape = syn.Shape(B=1, H=2, d=128, T=128, Nq=2 * 128 + 17, W=W, C=C, topk=topk)
+    _log(f"limits W={W} C={C} topk={topk}")
+    st = syn.make_state(shape, 13, pad_value=float("nan"), sigma=1.0, shift=1.0, n_planted=3,
+                        pool_count=[C, C // 2])
+    L, ref, ref_ws = _two_calls_then_fused(shape, st, None)
+    _assert_same(L, ref, ref_ws, f"W={W} C={C} topk={topk}")
+
+
 def test_select_attn_fwd_bad_pool_count_is_flagged():
     """A pool_count above C is clamped and flagged by the fused call as by
     the separate ones, with the same outputs."""
