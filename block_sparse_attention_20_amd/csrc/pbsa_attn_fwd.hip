@@ -867,12 +867,16 @@ constexpr int kSplitSlots = 512;
 // resident slots per query block are free).  More pieces keep more loads
 // in flight but each adds a partial to write and merge: forward on 1-4
 // query blocks x 12 heads of the Wan cache took 41-51 us (cold caches)
-// with 8, against 57-58 with 4 and 50-70 with 16.
+// with 8, against 57-58 with 4.  16 pieces pay off only while every piece
+// has a CU to itself (1 query block x 12 heads: 36 us against 39; at 2,
+// 43 against 40).
 constexpr int kMaxPieces = 8;
+constexpr int kMaxPiecesAlone = 16;
 // The fp32 path serves small problems, where a query block's list is a few
 // blocks: one piece per list entry, up to this many.
 constexpr int kMaxPiecesF32 = 16;
-static_assert(kMaxPieces <= kMergePieces && kMaxPiecesF32 <= kMergePieces,
+static_assert(kMaxPieces <= kMergePieces && kMaxPiecesAlone <= kMergePieces &&
+                  kMaxPiecesF32 <= kMergePieces,
               "the merge loads every piece's running max and row sum at once");
 
 static int split_slots() {
@@ -966,8 +970,11 @@ static FwdArgs fwd_args(const pbsa_problem &p, float scale, const void *q, const
 // traffic.  It needs at least two pieces of at least one list entry each
 // (a one-entry list is never split).
 static int64_t split_pieces(const pbsa_problem &p, const FwdArgs &a) {
-  int64_t pcs = split_slots() / a.n_items;
-  const int max_pieces = p.dtype == PBSA_BF16 ? kMaxPieces : kMaxPiecesF32;
+  const int64_t slots = split_slots();
+  int64_t pcs = slots / a.n_items;
+  int max_pieces = kMaxPiecesF32;
+  if (p.dtype == PBSA_BF16)
+    max_pieces = (int64_t)a.n_items * kMaxPiecesAlone <= slots / 2 ? kMaxPiecesAlone : kMaxPieces;
   if (pcs > max_pieces) pcs = max_pieces;
   if (pcs > a.NB) pcs = a.NB;
   return pcs;

@@ -185,7 +185,8 @@ int pbsa_block_mass(const pbsa_problem *p, float *mass_pool, float *mass_win, co
  * pbsa_workspace_size(p, PBSA_OP_FWD)) each query block runs in one
  * workgroup.  With a large enough 16-byte-aligned ws and at most half the
  * GPU's resident workgroups' worth of query blocks, every query block's list
- * is cut into 2 to 8 equal ranges (bf16; fp32: up to 16, at most one list
+ * is cut into 2 to 8 equal ranges (bf16: up to 16 while every piece can have
+ * a CU to itself; fp32: up to 16, at most one list
  * entry each), one workgroup each;
  * each piece leaves a partial in ws (fp32 O, running max and row sum of
  * its 2T threads; at most 512 pieces) and a second kernel, enqueued by the
