@@ -422,8 +422,9 @@ def small_chunks(torch, device="cuda", iters=20):
 
 
 def mass_compare(torch, n_chunks=16, n_layers=2, device="cuda"):
-    """Coarse vs exact (fine-grained) block mass as the Top-C score, and the
-    head-shared pool (one pool per layer, coarse masses summed over heads), on the
+    """Coarse vs exact (fine-grained) block mass as the Top-C score, the
+    head-shared pool (one pool per layer, coarse masses summed over heads)
+    and the sink policy (the first chunk's blocks pinned), on the
     streaming Wan-shaped rollout (pool cap 64, k = 16, 8 planted salient
     blocks per chunk): per chunk, the overlap of the two pools (Jaccard over
     (layer, head)); and for layer 0, with dense attention over the whole
@@ -443,6 +444,10 @@ def mass_compare(torch, n_chunks=16, n_layers=2, device="cuda"):
     # the head-shared pool variant: one pool per layer, coarse masses summed over heads
     ros["shared"] = Rollout(n_layers, s.B, s.H, s.d, s.T, s.Nq, C, s.topk, window_chunks=2,
                             device=device, overlap=True, shared_pool=True)
+    # the sink policy: the first chunk's blocks (ids 0 .. QB-1) pinned in the
+    # pool once they leave the window, the rest ranked by coarse mass
+    ros["sinks"] = Rollout(n_layers, s.B, s.H, s.d, s.T, s.Nq, C, s.topk, n_sink=qb,
+                           window_chunks=2, device=device, overlap=True)
     sigma = 1 / math.sqrt(s.d)
     hist = []  # layer 0's chunks: (k, v) padded to whole blocks, [B,H,QB,T,d]
     pad = qb * s.T - s.Nq
@@ -465,9 +470,10 @@ def mass_compare(torch, n_chunks=16, n_layers=2, device="cuda"):
         pools = {m: (ro.layers[0].t["pool_id"].clone(), ro.layers[0].t["pool_count"].clone())
                  for m, ro in ros.items()}
         ms, fwd_ms = {}, {}
-        # the three rollouts take turns at running first: the first one after
-        # an idle gap runs at a higher clock than the ones right behind it
-        order = list(ros)[t % 3:] + list(ros)[:t % 3]
+        # the rollouts take turns at running first: the first one after an
+        # idle gap runs at a higher clock than the ones right behind it
+        nr = len(ros)
+        order = list(ros)[t % nr:] + list(ros)[:t % nr]
         for m in order:
             ro = ros[m]
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -482,8 +488,8 @@ def mass_compare(torch, n_chunks=16, n_layers=2, device="cuda"):
             ms[m] = e0.elapsed_time(e1)
             fwd_ms[m] = sum(a.elapsed_time(b) for a, b in fe)
         row = {"chunk": t, "ms_coarse": round(ms["coarse"], 3), "ms_fine": round(ms["fine"], 3),
-               "ms_shared": round(ms["shared"], 3), "fwd_ms_coarse": round(fwd_ms["coarse"], 3),
-               "fwd_ms_fine": round(fwd_ms["fine"], 3)}
+               "ms_shared": round(ms["shared"], 3), "ms_sinks": round(ms["sinks"], 3),
+               "fwd_ms_coarse": round(fwd_ms["coarse"], 3), "fwd_ms_fine": round(fwd_ms["fine"], 3)}
         # pool overlap after this chunk's update
         jac = []
         for l in range(n_layers):
@@ -544,7 +550,8 @@ def mass_compare(torch, n_chunks=16, n_layers=2, device="cuda"):
         fwd_us = min(fwd_us, per_call_us(L.fwd))
         fwd_mass_us = min(fwd_mass_us, per_call_us(L.fwd_mass))
     return {"workload": f"streaming rollout, {n_chunks} chunks x {n_layers} layers, pool cap {C}, "
-                        "coarse vs exact block mass as the Top-C score, and a head-shared pool",
+                        "coarse vs exact block mass as the Top-C score, a head-shared pool and "
+                        "the first chunk's blocks as sinks",
             "per_chunk": rows, "fine_mass_us": fine_us, "fwd_us": fwd_us,
             "fwd_mass_us": fwd_mass_us,
             "fused_mass_extra_frac": round((fwd_mass_us - fwd_us) / fwd_us, 4)}
