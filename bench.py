@@ -158,7 +158,8 @@ def breakdown(ro, torch, reps=3):
 
 
 def train_step(torch, steps=5, warmup=2, device="cuda"):
-    """Batch-2 training step of one layer: select + fwd + bwd."""
+    """Batch-2 training step of one layer: routing + forward (one launch), then
+    the backward; fwd_ms is the routing + forward launch."""
     import pbsa_synth as syn
     from block_sparse_attention_20_amd.layer import PBSALayer
     from block_sparse_attention_20_amd.rollout import attended_tokens
@@ -170,14 +171,13 @@ def train_step(torch, steps=5, warmup=2, device="cuda"):
     dout = syn.make_dout(s, 4001, device=device)
     grads = None
     for _ in range(warmup):
-        L.select(); L.fwd(); grads = L.bwd(dout, grads)
+        L.select_fwd(); grads = L.bwd(dout, grads)
     torch.cuda.synchronize()
     ef = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     eb = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
-        L.select()
-        ef[i][0].record(); L.fwd(); ef[i][1].record()
+        ef[i][0].record(); L.select_fwd(); ef[i][1].record()
         eb[i][0].record(); grads = L.bwd(dout, grads); eb[i][1].record()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
@@ -185,7 +185,7 @@ def train_step(torch, steps=5, warmup=2, device="cuda"):
     fwd_ms = sum(a.elapsed_time(b) for a, b in ef) / steps
     bwd_ms = sum(a.elapsed_time(b) for a, b in eb) / steps
     fwd_f, bwd_f = 4 * s.d * pairs, 10 * s.d * pairs
-    return {"workload": "wan chunk training step, batch 2 (select + fwd + bwd, one layer)",
+    return {"workload": "wan chunk training step, batch 2 (routing + fwd in one launch, bwd; one layer)",
             "ms_per_step": round(ms, 4), "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
             "fwd_gflop": round(fwd_f / 1e9, 2), "bwd_gflop": round(bwd_f / 1e9, 2),
             "tflops": round((fwd_f + bwd_f) / (ms * 1e-3) / 1e12, 2),
