@@ -24,9 +24,10 @@
 //   4. dK/dV: one workgroup per stored KV block (pool slot, current block,
 //      window slot - the ones attended by every query block first), looping
 //      over the query blocks that attend it (all of them for pool and current
-//      blocks, the CSR list for window slots) in 64-row Q/dO tiles, DMA
-//      staged and double buffered; K and V stay in registers.  Blocks nobody
-//      attends get zeros.
+//      blocks, the CSR list for window slots) in 32-row Q/dO tiles, DMA
+//      staged and double buffered (separate buffers indexed at compile time,
+//      so no read waits for the next tile's DMA); K and V stay in
+//      registers.  Blocks nobody attends get zeros.
 // Every gradient element is written by exactly one workgroup, in a fixed
 // order, so results are bitwise reproducible.
 //
@@ -477,22 +478,29 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dq_kernel(BwdAr
 //    [pool C | current QB | window W].
 // ---------------------------------------------------------------------------
 
-// (L, -D) of query rows [r0, r0 + 64) into LD[0..127] (row r at 2r, 2r+1)
-// with one 1 KB buffer load by wave 0: lanes 0..31 move the 512 bytes, lanes
-// 32..63 are past the descriptor's range and write zeros to LD[128..255].
-__device__ __forceinline__ void dma_rows_ld(float *LD, const float *src, int lane) {
+// (L, -D) of query rows [r0, r0 + 32) into LD[0..63] (row r at 2r, 2r+1)
+// with one buffer load by wave 0: lanes 0..15 move the 256 bytes, lanes
+// 16..63 are past the descriptor's range and write zeros to LD[64..255].
+__device__ __forceinline__ void dma_rows_ld32(float *LD, const float *src, int lane) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(src), (short)0, 512, 0x00020000),
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(src), (short)0, 256, 0x00020000),
       (lds_void *)LD, 16, (uint32_t)lane * 16, 0, 0, 0);
 }
 
 template <int D, int BT>
 __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dkv_kernel(BwdArgs a) {
-  constexpr int NW = BT / 32, TT = kTileB;
-  using G = DmaGeom<D, TT, NW>;
-  __shared__ __attribute__((aligned(1024))) uint16_t Qb[2][TT * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Ob[2][TT * D];  // dO rows
-  __shared__ __attribute__((aligned(1024))) float LD[2][256];  // (L, -D) per row, 128..255 zero
+  // 32-row Q / dO tiles, two of the waves moving each (16 rows apiece);
+  // separate LDS arrays per buffer half, indexed at compile time, so that
+  // the compiler sees this tile's reads and the next tile's DMA touch
+  // different objects
+  constexpr int TT = 32, NWD = 2;
+  using G = DmaGeom<D, TT, NWD>;
+  __shared__ __attribute__((aligned(1024))) uint16_t Q0[TT * D], Q1[TT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t O0[TT * D], O1[TT * D];  // dO rows
+  __shared__ __attribute__((aligned(1024))) float LD0[256], LD1[256];  // (L, -D) per row, 64..255 zero
+  uint16_t *const Qb[2] = {Q0, Q1};
+  uint16_t *const Ob[2] = {O0, O1};
+  float *const LD[2] = {LD0, LD1};
   const int item = bwd_item(a);
   if (item >= a.n_items) return;
   const int nj = a.C + a.W + a.QB;
@@ -555,7 +563,7 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dkv_kernel(BwdA
     const int rbase = l32 * D + ((g ^ lds_swz<D, kSwzU>(l32)) * 8);
     const int tbase = tr_base<D>(lane);
     uint32_t rdma[G::NVAR];
-    dma_lane_offsets<D, TT, NW, kSwzU>(lane, rdma);
+    dma_lane_offsets<D, TT, NWD, kSwzU>(lane, rdma);
     const size_t NqP = (size_t)a.QB * BT;
 
     // query tile stream: list entry n (query block qi), half h
@@ -563,16 +571,21 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dkv_kernel(BwdA
     int qi = all_q ? 0 : __builtin_amdgcn_readfirstlane(ql[0]);
     int qlen = min(BT, a.Nq - qi * BT);
     int tlen = min(TT, qlen);
-    {
+    if (wave < NWD) {
       const size_t r0 = bh * a.Nq + (size_t)qi * BT;
-      TileDma<D, TT, NW>::tile(Qb[0], a.q + r0 * D, tlen, wave, rdma);
-      TileDma<D, TT, NW>::tile(Ob[0], a.dout + r0 * D, tlen, wave, rdma);
-      if (wave == 0) dma_rows_ld(LD[0], a.LDp + 2 * (bh * NqP + qi * BT), lane);
+      TileDma<D, TT, NWD>::tile(Qb[0], a.q + r0 * D, tlen, wave, rdma);
+      TileDma<D, TT, NWD>::tile(Ob[0], a.dout + r0 * D, tlen, wave, rdma);
+      if (wave == 0) dma_rows_ld32(LD[0], a.LDp + 2 * (bh * NqP + qi * BT), lane);
     }
-    int buf = 0;
-    while (true) {
+    int rb = rbase, tb = tbase;
+    auto step = [&](auto bufc) __attribute__((always_inline)) -> bool {
+      constexpr int buf = decltype(bufc)::value;
       PBSA_WAIT_VM(0);
       __syncthreads();
+      // per-step copies of the lane offsets: values derived from them are
+      // formed inside the step, not held across it
+      asm volatile("" : "+v"(rb), "+v"(tb));
+      const int rbase = rb, tbase = tb;
       int nn = n, hn = h + 1, qin = qi, qlenn = qlen, nlen = 0;
       if (hn * TT >= qlen || hn * TT >= BT) {
         nn = n + 1;
@@ -583,19 +596,19 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dkv_kernel(BwdA
         }
       }
       const bool more = nn < nq;
-      if (more) {
+      if (more && wave < NWD) {
         nlen = min(TT, qlenn - hn * TT);
         const size_t r0 = bh * a.Nq + (size_t)qin * BT + hn * TT;
-        TileDma<D, TT, NW>::tile(Qb[buf ^ 1], a.q + r0 * D, nlen, wave, rdma);
-        TileDma<D, TT, NW>::tile(Ob[buf ^ 1], a.dout + r0 * D, nlen, wave, rdma);
-        if (wave == 0) dma_rows_ld(LD[buf ^ 1], a.LDp + 2 * (bh * NqP + (size_t)qin * BT + hn * TT), lane);
+        TileDma<D, TT, NWD>::tile(Qb[buf ^ 1], a.q + r0 * D, nlen, wave, rdma);
+        TileDma<D, TT, NWD>::tile(Ob[buf ^ 1], a.dout + r0 * D, nlen, wave, rdma);
+        if (wave == 0) dma_rows_ld32(LD[buf ^ 1], a.LDp + 2 * (bh * NqP + (size_t)qin * BT + hn * TT), lane);
       }
+      if (more) nlen = min(TT, qlenn - hn * TT);
       const uint16_t *Ql = Qb[buf];
       const uint16_t *Ol = Ob[buf];
       const float *LDl = LD[buf];
-
-#pragma unroll 1
-      for (int qs = 0; qs < TT / 32; ++qs) {
+      {
+        constexpr int qs = 0;
         if (qs * 32 < tlen) {
           // S = Q K^T and dP = dO V^T over 32 query rows (element e of a
           // lane is query row 32 qs + 8 (e / 4) + 4 g + e % 4)
@@ -655,13 +668,15 @@ __global__ __launch_bounds__(2 * BT, BT == 128 ? 2 : 1) void bwd_dkv_kernel(BwdA
           }
         }
       }
-      if (!more) break;
+      if (!more) return false;
       n = nn;
       h = hn;
       qi = qin;
       qlen = qlenn;
       tlen = nlen;
-      buf ^= 1;
+      return true;
+    };
+    while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
     }
   }
   // this lane's token row.  Padding rows of stored slots get zeros: their
