@@ -133,3 +133,52 @@ def test_select_attn_fwd_requires_select_workspace():
     with pytest.raises(P.PBSAError) as e:
         P.pbsa_select_attn_fwd(L.prob, t["q"], L.kv, t["sel"], t["sel_count"], t["o"], t["lse"], None)
     assert e.value.code == P.PBSA_ERR_WORKSPACE
+
+
+def test_select_attn_fwd_and_static_select_replay_in_a_graph():
+    """The calls make no allocation and no memset, so a caller can capture
+    them: the one-launch routing + forward, and the allocation-free select
+    followed by the forward, captured in a HIP graph and replayed three
+    times (other work and synchronisation between replays) give the eager
+    results bit for bit every time."""
+    shape = syn.WAN_CHUNK
+    st = syn.wan_chunk_state(2)
+    L = PBSALayer(shape.B, shape.H, shape.d, shape.T, shape.Nq, shape.W, shape.C, shape.topk,
+                  device="cuda", ws_fwd=None).load(st)
+    t = L.t
+
+    def fused():
+        L.select_fwd()
+
+    def static_then_fwd():
+        P.pbsa_select_static(L.prob, t["q"], L.kv, t["sel"], t["sel_count"], None, None)
+        L.fwd()
+
+    for name, fn in (("fused", fused), ("static select + fwd", static_then_fwd)):
+        _log(f"graph replay: {name}")
+        fn()
+        torch.cuda.synchronize()
+        ref = {k: t[k].clone() for k in OUT_KEYS}
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            fn()  # warm-up on the capture stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for r in range(3):
+            for k in ("o", "lse"):
+                t[k].fill_(float("nan"))
+            t["sel"].fill_(-7)
+            t["sel_count"].fill_(-7)
+            g.replay()
+            torch.cuda.synchronize()
+            for k in OUT_KEYS:
+                assert torch.equal(t[k], ref[k]), (name, r, k)
+            fn()  # eager work between replays
+            torch.cuda.synchronize()
+        del g
+    assert L.status_bits() == 0
