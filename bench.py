@@ -46,8 +46,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # FETCH 14,167 KiB, WRITE 28,304 KiB).  Valid only for the kernel source it
 # was measured on (sha1 over FWD_SOURCES below); reported as null once those
 # sources change.
-FWD_TRAFFIC = {"src_sha1": "89e08321aac3f3077e54ef370930fe6418fa8479",
-               "fetch_kib": 64343.8, "write_kib": 15154.6,
+FWD_TRAFFIC = {"src_sha1": "9089b2d1527be3bd8512beb82987ec82e3ebc5c8",
+               "fetch_kib": 64153.8, "write_kib": 15156.4,
                "fetch_scale": 28302.0 / 14166.5, "write_scale": 28302.0 / 28304.3}
 
 
