@@ -43,10 +43,10 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # --pmc passes (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by
 # what the same counter reads for a copy kernel of known size (the window
 # append: 28,302 KiB read and 28,302 KiB written per launch; it reads back
-# FETCH 14,167 KiB, WRITE 28,304 KiB).  Valid only for the kernel source it
-# was measured on (sha1 over FWD_SOURCES below); reported as null once those
-# sources change.
-FWD_TRAFFIC = {"src_sha1": "9089b2d1527be3bd8512beb82987ec82e3ebc5c8",
+# FETCH 14,167 KiB, WRITE 28,304 KiB).  Valid only for the kernel code it
+# was measured on (sha1 over FWD_SOURCES below, comments left out); reported
+# as null once that code changes.
+FWD_TRAFFIC = {"src_sha1": "3ae10adffd1d1288c9f22f6a4b03c09a821cbc7c",
                "fetch_kib": 64153.8, "write_kib": 15156.4,
                "fetch_scale": 28302.0 / 14166.5, "write_scale": 28302.0 / 28304.3}
 
@@ -55,13 +55,19 @@ FWD_SOURCES = ("pbsa_attn_fwd.hip", "pbsa_tiles.h", "pbsa_select_dev.h")
 
 
 def fwd_source_sha1() -> str:
-    """sha1 over the forward kernel's sources (the kernel file and the
-    headers of tile staging and of the routing it runs first)."""
+    """sha1 over the forward kernel's code (the kernel file and the headers
+    of tile staging and of the routing it runs first), with comments and
+    blank lines left out, so that only a change of code invalidates it."""
     import hashlib
+    import re
     h = hashlib.sha1()
     for name in FWD_SOURCES:
-        with open(os.path.join(ROOT, "block_sparse_attention_20_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "block_sparse_attention_20_amd", "csrc", name)) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        for line in text.splitlines():
+            line = line.split("//", 1)[0].rstrip()
+            if line:
+                h.update(line.encode() + b"\n")
     return h.hexdigest()
 
 

@@ -56,10 +56,11 @@ struct FwdArgs {
   int32_t *status;
   int H, Nq, W, C, topk, QB, n_items, per_xcd;
   float sl2;  // scale * log2(e)
-  // balanced split: NB list entries per item, G workgroups sharing
-  // U = n_items * NB block visits; partial results of items cut between
-  // workgroups go to part_o / part_ml, and attn_fwd_merge_kernel combines
-  // them after the forward launch.
+  // NB: list entries per item (an upper bound: C + topk + QB).  Split
+  // launch (split = 1): every item's entries cut into P ranges, one per
+  // workgroup, G = n_items * P workgroups; each piece writes its partial to
+  // part_o / part_ml and attn_fwd_merge_kernel combines them after the
+  // forward launch.
   int split, NB, G;
   int P;  // pieces per query block in the split launch
   float *part_o, *part_ml;
